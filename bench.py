@@ -1,0 +1,266 @@
+"""Benchmark of the MXFP8 attention-forward hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input already resident in
+HBM: MXFP8-quantize Q and K (RCEIL), cast V to E4M3 (fp8 PV mode), and the fused attention
+forward. The packed-sequence metadata is built once, before timing (the LP-FA4 README's
+benchmark quantizes once and builds metadata up front; here quantization is inside the step
+and is also reported on its own).
+
+Prints ONE JSON line: value = attention FLOPs (4 * Lq * Lk * H * D summed over sequences)
+per second of whole step; roofline = the attention kernel's own rate from HIP events around
+each of its launches in the timed region, against the dense FP8 matrix peak; cpu_baseline =
+the float64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (AMD spec, no sparsity)
+BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOAD_TEXT = {
+    "tiny": "tiny: 1 sequence x 256 tokens, 2 heads, head_dim 128, noncausal MHA",
+    "dense": "dense: 1 sequence x 2048 tokens, 16 heads, head_dim 128, noncausal MHA",
+    "varlen": "varlen: 8 sequences, lengths uniform in [128, 4096] (seed 0), 16 heads, head_dim 128, 0.1% x20 outliers",
+    "pertensor": "pertensor: 2 x 16384 tokens, 24 heads, head_dim 128, per-tensor FP8 e4m3 (no descale)",
+    "cross": "cross: queries 4096 tokens, keys/values 32768 tokens, 16 heads, head_dim 128, keys N(0, 0.25)",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="dense", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--pv-mode", default="fp8", choices=["bf16", "fp8"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows per head in the oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_traffic.json"),
+                    help="measured HBM bytes per attention launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_attention_mxfp8_amd as lp
+    from synth import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = lp.load_library()   # fails loudly if the HIP library is missing
+
+    wl = make_workload(args.workload, seed=args.seed)
+    pv_mode = args.pv_mode
+    mq = lp.VarlenMeta.from_lengths(wl.lengths_q, dev)
+    mk = lp.VarlenMeta.from_lengths(wl.lengths_k, dev)
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(wl.q_bits), up(wl.k_bits), up(wl.v_bits)
+    flops = wl.flops()
+    per_tensor = args.workload == "pertensor"
+    if per_tensor:
+        pv_mode = "fp8"
+    order = lp.longest_first_tile_order(mq, mk, wl.num_heads) if args.workload == "varlen" else None
+
+    # outputs preallocated once; the step writes into them
+    out = torch.empty((mq.total_tokens, wl.num_heads, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.num_heads, mq.total_tokens), dtype=torch.float32, device=dev)
+    state = {}
+
+    def step():
+        if per_tensor:
+            qx, kx = lp.cast_e4m3(q), lp.cast_e4m3(k)
+        else:
+            qx = lp.quantize_mxfp8_varlen(q, mq)
+            kx = lp.quantize_mxfp8_varlen(k, mk)
+        vx = lp.cast_e4m3(v) if pv_mode == "fp8" else v
+        state["ops"] = (qx, kx, vx)
+        ev = state.get("ev")
+        if ev is not None:
+            ev[0].record()
+        lp.lp_attn_varlen_fwd(qx, kx, vx, mq, mk, pv_mode=pv_mode, tile_order=order, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+
+    log(f"workload {args.workload} pv_mode {pv_mode}: {flops / 1e9:.2f} GFLOP per forward")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps; HIP events bracket every attention launch ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        state["ev"] = evs[i]
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    state["ev"] = None
+    step_ms = start.elapsed_time(stop) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_ms = float(np.mean(attn_ms))
+    attn_med_ms = float(np.median(attn_ms))
+    log(f"step {step_ms * 1e3:.2f} us (wall {wall / args.steps * 1e6:.2f} us), attention avg {attn_avg_ms * 1e3:.2f} us "
+        f"median {attn_med_ms * 1e3:.2f} us")
+
+    # ---- attention back-to-back (the pages' protocol: quantize once, time the forward) ----
+    qx, kx, vx = state["ops"]
+    n_b2b = max(10, min(2000, int(0.5 / max(attn_avg_ms * 1e-3, 1e-6))))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n_b2b):
+        lp.lp_attn_varlen_fwd(qx, kx, vx, mq, mk, pv_mode=pv_mode, tile_order=order, out=out, lse=lse)
+    b.record()
+    torch.cuda.synchronize()
+    b2b_ms = a.elapsed_time(b) / n_b2b
+
+    # ---- quantizer alone: Q and K back to back ----
+    quant_gbps = None
+    if not per_tensor:
+        n_q = 200
+        a.record()
+        for _ in range(n_q):
+            lp.quantize_mxfp8_varlen(q, mq)
+            lp.quantize_mxfp8_varlen(k, mk)
+        b.record()
+        torch.cuda.synchronize()
+        qms = a.elapsed_time(b) / n_q
+        qbytes = sum(t.numel() * 2 + t.numel() + m.total_scale_rows * wl.num_heads * 4
+                     for t, m in ((q, mq), (k, mk)))
+        quant_gbps = qbytes / (qms * 1e-3) / 1e9
+
+    # ---- pv bf16 variant of the same workload, for the record ----
+    extra = {}
+    if not per_tensor and pv_mode == "fp8":
+        a.record()
+        for _ in range(n_b2b):
+            lp.lp_attn_varlen_fwd(qx, kx, v, mq, mk, pv_mode="bf16", tile_order=order, out=out, lse=lse)
+        b.record()
+        torch.cuda.synchronize()
+        bf_ms = a.elapsed_time(b) / n_b2b
+        extra["attention_pv_bf16_tflops"] = round(flops / (bf_ms * 1e-3) / 1e12, 2)
+
+    achieved = flops / (attn_avg_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            key = f"{args.workload}/{pv_mode}"
+            if key in tj and tj[key].get("kernel_source_hash") == kernel_source_hash():
+                traffic = tj[key]["bytes_per_launch"]
+        except Exception as e:  # pragma: no cover
+            log(f"traffic file unreadable: {e}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, pv_mode, args.cpu_rows, per_tensor)
+
+    line = {
+        "metric": "MXFP8 attention fwd TFLOP/s (1 GPU) + % of FP8 MFMA peak; quantizer GB/s",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3" if pv_mode == "fp8" else "fp8e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "pv_mode": pv_mode,
+                   "scaling_mode": "rceil" if not per_tensor else "per-tensor",
+                   "seq_lens_q": list(wl.lengths_q)[:16], "seq_lens_k": list(wl.lengths_k)[:16],
+                   "heads": wl.num_heads, "head_dim": 128, "seed": args.seed,
+                   "step": "quantize Q,K + cast V + attention forward" if not per_tensor
+                   else "cast Q,K,V + attention forward"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "attention_kernel_tflops_b2b": round(flops / (b2b_ms * 1e-3) / 1e12, 2),
+        "attention_kernel_us_avg": round(attn_avg_ms * 1e3, 3),
+        "attention_kernel_us_median": round(attn_med_ms * 1e3, 3),
+        "quantizer_gbps": None if quant_gbps is None else round(quant_gbps, 1),
+        "pct_fp8_peak": round(100 * achieved / FP8_PEAK_TFLOPS, 2),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "precision_attention_mxfp8_amd", "csrc", "attn_fwd.hip")
+    h.update(open(src, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, pv_mode, rows_per_head, per_tensor):
+    """The float64 oracle on a bounded sample: quantize Q and K in full, then attention for
+    `rows_per_head` evenly spaced query rows of each sequence and head against all keys."""
+    import oracle
+    from synth import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    xq = bf16_bits_to_f32(wl.q_bits).astype(np.float64)
+    xk = bf16_bits_to_f32(wl.k_bits).astype(np.float64)
+    xv = bf16_bits_to_f32(wl.v_bits).astype(np.float64)
+    if per_tensor:
+        qh, kh = oracle.e4m3_decode(oracle.e4m3_encode(xq)), oracle.e4m3_decode(oracle.e4m3_encode(xk))
+    else:
+        pq, sq, cq = oracle.mx_quantize_varlen(xq, wl.cu_q)
+        pk, sk, ck = oracle.mx_quantize_varlen(xk, wl.cu_k)
+        qh = oracle.mx_dequantize_varlen(pq, sq, wl.cu_q, cq)
+        kh = oracle.mx_dequantize_varlen(pk, sk, wl.cu_k, ck)
+    vp = oracle.e4m3_decode(oracle.e4m3_cast(xv)) if pv_mode == "fp8" else xv
+    rows = {r: np.linspace(0, lq - 1, min(rows_per_head, lq)).astype(np.int64)
+            for r, lq in enumerate(wl.lengths_q) if lq > 0}
+    oracle.attention_varlen(qh, kh, vp, wl.cu_q, wl.cu_k, pv_mode=pv_mode, rows=rows)
+    dt = time.perf_counter() - t0
+    sample_flops = sum(4 * len(rows[r]) * wl.lengths_k[r] * wl.num_heads * 128 for r in rows)
+    return {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(threads, cores)),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle: full MXFP8 quantize of Q and K, then attention for {rows_per_head} "
+                      f"query rows per (sequence, head) against all keys ({sample_flops / 1e9:.2f} GFLOP); "
+                      f"{dt:.1f} s wall; host affinity {cores} cores"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * lpfa.h - C ABI of the MXFP8 attention-forward library for AMD Instinct MI355X (gfx950).
+ *
+ * The library does two things, both on the GPU, both on a stream the caller owns:
+ *   1. MXFP8 quantization of packed variable-length (tokens, heads, 128) tensors:
+ *      E4M3 payloads plus one E8M0 scale per 32-element block along head_dim, each
+ *      sequence with its own scale storage padded to a multiple of 128 tokens
+ *      (LP-FA4 README, section "MXFP8 forward and backward"), and the unscaled E4M3
+ *      cast of V used by the fp8 PV mode (FastVideo PR "fp8 PV mode for the FA4-FP4
+ *      attention path", description of the fa4_v_to_fp8 op).
+ *   2. A fused noncausal head_dim-128 attention forward over packed sequences
+ *      (LP-FA4 README, introduction: dense attention is uniform packed offsets),
+ *      S = Q K^T on block-scaled E4M3 operands, online softmax, then P V with V in
+ *      BF16 or unscaled E4M3, writing O in BF16 and the log-sum-exp in FP32.
+ *      Optional per-tensor q/k/v descales; a missing descale is read as 1.0 with the
+ *      same arithmetic, so a unit descale gives bit-identical output (vLLM PR
+ *      "FA4: no FP8 descale for a unit per-tensor scale", sections "Claims" and
+ *      "Validation").
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers to memory the caller allocated; the
+ *     library never allocates, frees or synchronises, and launches only on `stream`
+ *     (a hipStream_t passed as void*; NULL means the default stream).
+ *   - Strides are in elements. Element types: BF16 = raw uint16 bit patterns,
+ *     E4M3 / E8M0 = uint8 codes, FP32 = float.
+ *   - Return value: LPFA_OK (0) or a negative code. On error nothing is launched,
+ *     and lpfa_last_error() describes the problem. All argument checks run on the
+ *     host and read no device memory; device-resident offsets (cu_seqlens, cu_scale)
+ *     are trusted, so their consistency is the caller's duty.
+ *   - Launch failures return LPFA_EIO; faults inside a kernel surface at the
+ *     caller's next synchronisation, as for any asynchronous launch.
+ *   - Entry points are thread-safe; concurrent calls on different streams do not
+ *     share state.
+ */
+#ifndef LPFA_H
+#define LPFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LPFA_ABI_VERSION 1
+
+#define LPFA_OK 0
+#define LPFA_EIO (-5)      /* kernel launch failed */
+#define LPFA_EINVAL (-22)  /* bad pointer, size, stride, alignment or enum value */
+#define LPFA_ENOTSUP (-95) /* well-formed but outside what the kernels implement */
+
+#define LPFA_DTYPE_BF16 0
+#define LPFA_DTYPE_FP32 1
+
+#define LPFA_SCALING_RCEIL 0 /* default: smallest e with amax <= 448 * 2^e */
+#define LPFA_SCALING_FLOOR 1 /* e = floor(log2 amax) - 8 */
+
+#define LPFA_PV_BF16 0 /* V is BF16 (default mode, behaviour unchanged) */
+#define LPFA_PV_FP8 1  /* V is unscaled E4M3, implicit dequant scale 1.0 */
+
+/* Version of this ABI (LPFA_ABI_VERSION of the built library). */
+int lpfa_abi_version(void);
+
+/* Message of the last error returned on the calling thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char* lpfa_last_error(void);
+
+/*
+ * mxfp8_quantize_varlen - MXFP8 quantization of a packed varlen tensor.
+ * (LP-FA4 README, section "MXFP8 forward and backward": E4M3 payload with one E8M0
+ *  scale per 32 elements, per-sequence 128-token-padded scale storage, RCEIL default,
+ *  FLOOR optional.)
+ *
+ * For every token t of sequence i, head h and 32-element block b of head_dim:
+ *   amax = max |x| over the block; e = RCEIL or FLOOR exponent of amax, clamped to
+ *   [-127, 127] (e = -127 for an all-zero block); scales[row, h, b] = e + 127;
+ *   payload[t, h, 32b + j] = E4M3(x * 2^-e) rounded to nearest even, saturating at 448.
+ *   row = cu_scale[i] + (t - cu_seqlens[i]).
+ * Scale rows from L_i to P(L_i)-1 of each sequence (P(L) = L rounded up to a multiple
+ * of 128) are pad rows and are written as 0x7F.
+ *
+ *   x            input, x[t * stride_tok + h * stride_head + d], d = 0..127 contiguous.
+ *                BF16 or FP32 (x_dtype). x and both strides times the element size
+ *                must be multiples of 16 bytes. Values must be finite.
+ *   total_tokens T = cu_seqlens[num_seqs]; num_heads >= 1; head_dim must be 128.
+ *   cu_seqlens   device int32[num_seqs + 1], 0 = cu_seqlens[0] <= ... (packed offsets).
+ *   cu_scale     device int32[num_seqs + 1], prefix sums of P(L_i).
+ *   total_scale_rows  cu_scale[num_seqs].
+ *   payload      output uint8 (T, num_heads, 128), contiguous.
+ *   scales       output uint8 (total_scale_rows, num_heads, 4), contiguous.
+ * Errors: LPFA_EINVAL for NULL pointers (unless the tensor is empty), negative sizes,
+ * misalignment, bad enum values; LPFA_ENOTSUP for head_dim != 128.
+ */
+int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                          int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                          const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
+                          int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
+                          uint8_t* scales, void* stream);
+
+/*
+ * lp_fp8_cast_e4m3 - unscaled E4M3 cast (the fp8 PV mode's V).
+ * (FastVideo PR "fp8 PV mode for the FA4-FP4 attention path": an elementwise e4m3 cast
+ *  of V with no scale factors; the attention reads it with dequant scale 1.0.)
+ *
+ *   y[t, h, d] = E4M3(x[t * stride_tok + h * stride_head + d]), nearest even,
+ *   saturating finite values above 448 to +-448 (sign kept, so -0 and negative
+ *   underflow give 0x80).
+ *   x: BF16 or FP32, 16-byte aligned with 16-byte-multiple strides; y: uint8
+ *   (total_tokens, num_heads, 128) contiguous. head_dim must be 128.
+ */
+int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                     int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
+                     void* stream);
+
+/*
+ * Arguments of lp_attn_varlen_fwd. Zero-initialise, then set struct_size =
+ * sizeof(lpfa_attn_args); fields added by later ABI versions go at the end.
+ */
+typedef struct lpfa_attn_args {
+  int32_t struct_size;
+
+  /* Q and K: E4M3 payloads, (total_q | total_k, num_heads, 128) with token/head strides
+   * in elements (head_dim contiguous; pointer and strides 16-byte multiples). */
+  const uint8_t* q;
+  const uint8_t* k;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+
+  /* MX block scales, uint8 (cu_scale_*[num_seqs], num_heads, 4) contiguous. Both set:
+   * block-scaled QK^T (the LP-FA4 MXFP8 forward). Both NULL: per-tensor FP8 mode
+   * (every block scale reads as 1.0). One without the other is LPFA_EINVAL. */
+  const uint8_t* q_scale;
+  const uint8_t* k_scale;
+  const int32_t* cu_scale_q; /* device int32[num_seqs + 1]; required with q_scale */
+  const int32_t* cu_scale_k;
+
+  /* V: BF16 (pv_mode LPFA_PV_BF16) or E4M3 (LPFA_PV_FP8), (total_k, num_heads, 128). */
+  const void* v;
+  int64_t v_stride_tok, v_stride_head;
+  int32_t pv_mode;
+
+  /* Packed sequence offsets (device int32[num_seqs + 1]); queries of sequence r attend
+   * to the keys of sequence r only. max_seqlen_q bounds every query length. */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t num_seqs;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int64_t total_q;
+  int64_t total_k;
+  int32_t num_heads; /* queries and keys have the same head count (MHA) */
+  int32_t head_dim;  /* must be 128 */
+
+  /* Softmax scale on the scores (callers usually pass 1/sqrt(128)); must be finite, > 0. */
+  float softmax_scale;
+  int32_t causal; /* must be 0: only noncausal attention is implemented */
+
+  /* Optional per-tensor descales, fp32, element [seq * stride_seq + head * stride_head]
+   * (strides may be 0 for broadcast). NULL reads as 1.0 through the same arithmetic.
+   * Scores are multiplied by q_descale * k_descale, O by v_descale. */
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  int64_t q_descale_stride_seq, q_descale_stride_head;
+  int64_t k_descale_stride_seq, k_descale_stride_head;
+  int64_t v_descale_stride_seq, v_descale_stride_head;
+
+  /* Outputs: O BF16 (total_q, num_heads, 128) contiguous; LSE fp32 (num_heads, total_q),
+   * natural log of the sum of exp of the scaled scores. A sequence with queries but no
+   * keys gets O = 0 and LSE = -inf. */
+  uint16_t* out;
+  float* lse;
+
+  /* Optional work order: device int32[3 * num_tiles] triples (seq, head, q_tile) of
+   * 128-query tiles, launched in this order (e.g. longest sequences first). NULL: every
+   * (seq, head, tile) in a default order. Each triple must be listed at most once. */
+  const int32_t* tile_order;
+  int32_t num_tiles;
+} lpfa_attn_args;
+
+/*
+ * lp_attn_varlen_fwd - fused noncausal attention forward over packed sequences.
+ * (LP-FA4 README, sections "MXFP8 forward and backward" and introduction; FastVideo
+ *  fp8-PV PR; vLLM unit-descale PR.)
+ *
+ * For sequence r, head h, query i and key j:
+ *   s_ij = softmax_scale * qd * kd * sum_b 2^(eq_ib + ek_jb) * sum_{d in b} q_id k_jd
+ *   (eq, ek = 0 in per-tensor mode), running row max m and sum l over key blocks
+ *   (online softmax), P rounded to V's type (BF16, or E4M3 with no scale), O_i =
+ *   vd * (sum_j P_ij V_j) / l_i rounded to BF16, LSE_i = ln sum_j exp(s_ij).
+ * Errors: LPFA_EINVAL (NULL pointers, bad strides/alignment, scale presence mismatch,
+ * v_descale with BF16 V, bad pv_mode, struct_size too small, non-positive scale);
+ * LPFA_ENOTSUP (head_dim != 128, causal != 0); LPFA_EIO (launch failure).
+ */
+int lp_attn_varlen_fwd(const lpfa_attn_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LPFA_H */

@@ -1,0 +1,268 @@
+"""Python binding of liblpfa: argument marshalling only, every step runs in the HIP kernels.
+
+PyTorch provides device memory and the current stream; the library launches on that
+stream and never allocates. The names follow the LP-FA4 README (section "MXFP8 forward
+and backward"): ``VarlenMeta.from_lengths`` builds the packed-sequence metadata once on the
+host, ``quantize_mxfp8_varlen`` makes the E4M3 payload plus per-32 E8M0 scales with
+128-token-padded per-sequence scale storage, and ``lp_attn_varlen_fwd`` returns
+``(out, lse)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 128
+PAD = 128
+
+Descale = Union[None, float, torch.Tensor]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class VarlenMeta:
+    """Packed variable-length metadata, built once from host lengths (dense = one uniform length).
+
+    ``cu_seqlens`` are packed token offsets, ``cu_scale`` the offsets of each sequence's
+    scale rows (each sequence padded to a multiple of 128 tokens).
+    """
+
+    lengths: Tuple[int, ...]
+    cu_seqlens_host: Tuple[int, ...]
+    cu_scale_host: Tuple[int, ...]
+    cu_seqlens: torch.Tensor
+    cu_scale: torch.Tensor
+    device: torch.device = field(repr=False, default=None)
+
+    @classmethod
+    def from_lengths(cls, lengths: Sequence[int], device="cuda") -> "VarlenMeta":
+        lengths = tuple(int(v) for v in lengths)
+        if any(v < 0 for v in lengths):
+            raise ValueError("sequence lengths must be non-negative")
+        cu, cs = [0], [0]
+        for v in lengths:
+            cu.append(cu[-1] + v)
+            cs.append(cs[-1] + -(-v // PAD) * PAD)
+        if cu[-1] >= 2 ** 31 or cs[-1] >= 2 ** 31:
+            raise ValueError("packed length exceeds int32 offsets")
+        dev = torch.device(device)
+        return cls(lengths, tuple(cu), tuple(cs),
+                   torch.tensor(cu, dtype=torch.int32, device=dev),
+                   torch.tensor(cs, dtype=torch.int32, device=dev), dev)
+
+    @classmethod
+    def dense(cls, batch: int, seqlen: int, device="cuda") -> "VarlenMeta":
+        """Dense (batch, seqlen) attention as uniform packed offsets."""
+        return cls.from_lengths([seqlen] * batch, device)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def total_tokens(self) -> int:
+        return self.cu_seqlens_host[-1]
+
+    @property
+    def total_scale_rows(self) -> int:
+        return self.cu_scale_host[-1]
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.lengths) if self.lengths else 0
+
+
+@dataclass
+class Mxfp8Tensor:
+    """MXFP8 operand: E4M3 payload (T, H, 128) uint8 and E8M0 scales (sum P(L_i), H, 4) uint8."""
+
+    payload: torch.Tensor
+    scales: torch.Tensor
+    meta: VarlenMeta
+
+
+def _check_rows(x: torch.Tensor, name: str) -> None:
+    if x.dim() != 3 or x.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be (tokens, heads, {HEAD_DIM}), got {tuple(x.shape)}")
+    if x.stride(2) != 1:
+        raise ValueError(f"{name} must be contiguous along head_dim")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str = "rceil") -> Mxfp8Tensor:
+    """MXFP8-quantize packed (tokens, heads, 128) BF16/FP32 ``x`` (RCEIL default, FLOOR optional)."""
+    if scaling_mode not in _lib.SCALING:
+        raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
+    _check_rows(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bfloat16 or float32")
+    if x.shape[0] != meta.total_tokens:
+        raise ValueError(f"x has {x.shape[0]} tokens, metadata says {meta.total_tokens}")
+    lib = _lib.load()
+    t, h, _ = x.shape
+    payload = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((meta.total_scale_rows, h, 4), dtype=torch.uint8, device=x.device)
+    rc = lib.mxfp8_quantize_varlen(
+        _ptr(x), _lib.DTYPE_BF16 if x.dtype == torch.bfloat16 else _lib.DTYPE_FP32,
+        x.stride(0), x.stride(1), t, h, HEAD_DIM, _ptr(meta.cu_seqlens), _ptr(meta.cu_scale),
+        meta.num_seqs, meta.total_scale_rows, _lib.SCALING[scaling_mode], _ptr(payload), _ptr(scales),
+        _stream())
+    _lib.check("mxfp8_quantize_varlen", rc)
+    return Mxfp8Tensor(payload, scales, meta)
+
+
+def cast_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """Unscaled E4M3 cast (fp8 PV mode's V): uint8 codes, same (tokens, heads, 128) shape, contiguous."""
+    _check_rows(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bfloat16 or float32")
+    lib = _lib.load()
+    t, h, _ = x.shape
+    y = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
+    rc = lib.lp_fp8_cast_e4m3(_ptr(x), _lib.DTYPE_BF16 if x.dtype == torch.bfloat16 else _lib.DTYPE_FP32,
+                              x.stride(0), x.stride(1), t, h, HEAD_DIM, _ptr(y), _stream())
+    _lib.check("lp_fp8_cast_e4m3", rc)
+    return y
+
+
+def _as_codes(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError("FP8 operands must be uint8 codes or torch.float8_e4m3fn")
+    return t
+
+
+def _descale(d: Descale, num_seqs: int, heads: int, device) -> Tuple[Optional[torch.Tensor], int, int]:
+    """A descale as (device fp32 tensor or None, stride over sequences, stride over heads).
+
+    A host float equal to 1.0 becomes None (no descale): the kernel reads a missing descale
+    as 1.0 through the same arithmetic, so this changes no bit of the output.
+    """
+    if d is None:
+        return None, 0, 0
+    if isinstance(d, (int, float)):
+        if float(d) == 1.0:
+            return None, 0, 0
+        return torch.full((1, 1), float(d), dtype=torch.float32, device=device), 0, 0
+    if not d.is_cuda or d.dtype != torch.float32:
+        raise ValueError("descale tensors must be float32 GPU tensors")
+    if d.dim() == 0:
+        d = d.reshape(1, 1)
+    if d.dim() != 2 or d.shape[0] not in (1, num_seqs) or d.shape[1] not in (1, heads):
+        raise ValueError(f"descale must broadcast to (num_seqs={num_seqs}, heads={heads}), got {tuple(d.shape)}")
+    s_seq = 0 if d.shape[0] == 1 else d.stride(0)
+    s_head = 0 if d.shape[1] == 1 else d.stride(1)
+    return d, s_seq, s_head
+
+
+def longest_first_tile_order(meta_q: VarlenMeta, meta_k: VarlenMeta, heads: int) -> torch.Tensor:
+    """Work order of 128-query tiles, most keys first, built once on the host from the lengths."""
+    tiles = []
+    for r, (lq, lk) in enumerate(zip(meta_q.lengths, meta_k.lengths)):
+        for qt in range(-(-lq // 128)):
+            for h in range(heads):
+                tiles.append((lk, r, h, qt))
+    tiles.sort(key=lambda t: (-t[0], t[1], t[3], t[2]))
+    flat: List[int] = [v for _, r, h, qt in tiles for v in (r, h, qt)]
+    return torch.tensor(flat, dtype=torch.int32, device=meta_q.device)
+
+
+def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor, torch.Tensor],
+                       v: torch.Tensor, meta_q: VarlenMeta, meta_k: VarlenMeta, pv_mode: str = "bf16",
+                       softmax_scale: Optional[float] = None, q_descale: Descale = None,
+                       k_descale: Descale = None, v_descale: Descale = None,
+                       tile_order: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Noncausal head_dim-128 attention forward over packed sequences -> (out BF16 (Tq,H,128), lse FP32 (H,Tq)).
+
+    ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T) or raw E4M3 codes (per-tensor FP8 mode).
+    ``v`` is BF16 for ``pv_mode="bf16"`` or E4M3 codes for ``pv_mode="fp8"`` (unscaled, see
+    :func:`cast_e4m3`). Descales are floats or fp32 tensors broadcastable to (num_seqs, heads).
+    """
+    if pv_mode not in _lib.PV_MODES:
+        raise ValueError(f"pv_mode must be one of {sorted(_lib.PV_MODES)}, got {pv_mode!r}")
+    mx_q, mx_k = isinstance(q, Mxfp8Tensor), isinstance(k, Mxfp8Tensor)
+    if mx_q != mx_k:
+        raise ValueError("q and k must both be Mxfp8Tensor (MX mode) or both raw E4M3 (per-tensor mode)")
+    qp = q.payload if mx_q else _as_codes(q)
+    kp = k.payload if mx_k else _as_codes(k)
+    _check_rows(qp, "q")
+    _check_rows(kp, "k")
+    _check_rows(v, "v")
+    if pv_mode == "bf16" and v.dtype != torch.bfloat16:
+        raise ValueError("pv_mode='bf16' needs a bfloat16 V")
+    if pv_mode == "fp8":
+        v = _as_codes(v)
+    if meta_q.num_seqs != meta_k.num_seqs:
+        raise ValueError("query and key metadata have different sequence counts")
+    for lq, lk in zip(meta_q.lengths, meta_k.lengths):
+        if lq > 0 and lk == 0:
+            raise ValueError("a sequence with queries must have at least one key")
+    tq, h, _ = qp.shape
+    tk = kp.shape[0]
+    if tq != meta_q.total_tokens or tk != meta_k.total_tokens or v.shape[0] != tk:
+        raise ValueError("tensor token counts do not match the metadata")
+    if kp.shape[1] != h or v.shape[1] != h:
+        raise ValueError("q, k and v must have the same number of heads")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    dev = qp.device
+    if out is None:
+        out = torch.empty((tq, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((h, tq), dtype=torch.float32, device=dev)
+    if out.shape != (tq, h, HEAD_DIM) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 (Tq, H, 128) tensor")
+    if lse.shape != (h, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (H, Tq) tensor")
+
+    qd, qss, qsh = _descale(q_descale, meta_q.num_seqs, h, dev)
+    kd, kss, ksh = _descale(k_descale, meta_q.num_seqs, h, dev)
+    vd, vss, vsh = _descale(v_descale, meta_q.num_seqs, h, dev)
+
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.q, a.k = _ptr(qp), _ptr(kp)
+    a.q_stride_tok, a.q_stride_head = qp.stride(0), qp.stride(1)
+    a.k_stride_tok, a.k_stride_head = kp.stride(0), kp.stride(1)
+    if mx_q:
+        a.q_scale, a.k_scale = _ptr(q.scales), _ptr(k.scales)
+        a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
+    a.v = _ptr(v)
+    a.v_stride_tok, a.v_stride_head = v.stride(0), v.stride(1)
+    a.pv_mode = _lib.PV_MODES[pv_mode]
+    a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
+    a.num_seqs = meta_q.num_seqs
+    a.max_seqlen_q, a.max_seqlen_k = meta_q.max_seqlen, meta_k.max_seqlen
+    a.total_q, a.total_k = tq, tk
+    a.num_heads, a.head_dim = h, HEAD_DIM
+    a.softmax_scale = float(softmax_scale)
+    a.causal = 0
+    a.q_descale, a.k_descale, a.v_descale = _ptr(qd), _ptr(kd), _ptr(vd)
+    a.q_descale_stride_seq, a.q_descale_stride_head = qss, qsh
+    a.k_descale_stride_seq, a.k_descale_stride_head = kss, ksh
+    a.v_descale_stride_seq, a.v_descale_stride_head = vss, vsh
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    if tile_order is not None:
+        if tile_order.dtype != torch.int32 or not tile_order.is_cuda or tile_order.numel() % 3:
+            raise ValueError("tile_order must be a GPU int32 tensor of (seq, head, tile) triples")
+        a.tile_order, a.num_tiles = _ptr(tile_order), tile_order.numel() // 3
+    rc = _lib.load().lp_attn_varlen_fwd(ctypes.byref(a), _stream())
+    _lib.check("lp_attn_varlen_fwd", rc)
+    return out, lse

@@ -1,0 +1,108 @@
+// C ABI entry points (include/lpfa.h): host checks, then one launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "kernels.h"
+#include "lpfa.h"
+#include "validate.h"
+
+namespace {
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LPFA_OK;
+  lpfa::set_error(std::string(what) + " launch failed: " + hipGetErrorString(e));
+  return LPFA_EIO;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lpfa_abi_version(void) { return LPFA_ABI_VERSION; }
+
+const char* lpfa_last_error(void) { return lpfa::last_error(); }
+
+int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                          int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                          const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
+                          int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
+                          uint8_t* scales, void* stream) {
+  if (int rc = lpfa::check_quantize(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads,
+                                    head_dim, cu_seqlens, cu_scale, num_seqs, total_scale_rows,
+                                    scaling_mode, payload, scales))
+    return rc;
+  lpfa::QuantParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.scaling_mode = scaling_mode;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.num_heads = num_heads;
+  p.num_seqs = num_seqs;
+  p.total_scale_rows = total_scale_rows;
+  p.cu_seqlens = cu_seqlens;
+  p.cu_scale = cu_scale;
+  p.payload = payload;
+  p.scales = scales;
+  return launch_status(lpfa::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize");
+}
+
+int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                     int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
+                     void* stream) {
+  if (int rc = lpfa::check_cast(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads, head_dim, y))
+    return rc;
+  lpfa::CastParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.total_tokens = total_tokens;
+  p.num_heads = num_heads;
+  p.y = y;
+  return launch_status(lpfa::launch_cast(p, static_cast<hipStream_t>(stream)), "e4m3 cast");
+}
+
+int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
+  if (int rc = lpfa::check_attn(a)) return rc;
+  lpfa::AttnParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.q_scale = a->q_scale;
+  p.k_scale = a->k_scale;
+  p.cu_scale_q = a->cu_scale_q;
+  p.cu_scale_k = a->cu_scale_k;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.q_descale = a->q_descale;
+  p.k_descale = a->k_descale;
+  p.v_descale = a->v_descale;
+  p.tile_order = a->tile_order;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.k_sh = a->k_stride_head;
+  p.v_st = a->v_stride_tok;
+  p.v_sh = a->v_stride_head;
+  p.qd_ss = a->q_descale_stride_seq;
+  p.qd_sh = a->q_descale_stride_head;
+  p.kd_ss = a->k_descale_stride_seq;
+  p.kd_sh = a->k_descale_stride_head;
+  p.vd_ss = a->v_descale_stride_seq;
+  p.vd_sh = a->v_descale_stride_head;
+  p.total_q = a->total_q;
+  p.num_heads = a->num_heads;
+  p.num_seqs = a->num_seqs;
+  p.q_tiles = (a->max_seqlen_q + 127) / 128;
+  p.num_tiles = a->tile_order ? a->num_tiles : a->num_seqs * a->num_heads * p.q_tiles;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  return launch_status(lpfa::launch_attention(p, a->q_scale != nullptr, a->pv_mode, static_cast<hipStream_t>(stream)),
+                       "attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Device-side helpers shared by the gfx950 kernels: vector types and the two hardware
+// conversions the path relies on (float -> E4M3 pair, float -> BF16), both round to
+// nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lpfa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Two floats -> two E4M3 codes in the low 16 bits (first value in the low byte).
+// The hardware conversion is OCP E4M3FN with round-to-nearest-even; magnitudes above
+// 464 would become NaN, so callers clamp to +-448 first when the input can exceed it.
+__device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four floats -> four E4M3 codes packed little-endian in one word.
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+
+// Two floats -> two BF16 (round to nearest even) packed in one word, first in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  uint16_t ua = __builtin_bit_cast(uint16_t, ha), ub = __builtin_bit_cast(uint16_t, hb);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace lpfa

@@ -1,0 +1,63 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lpfa.h"
+
+namespace lpfa {
+
+struct QuantParams {
+  const void* x;
+  int x_dtype;
+  int scaling_mode;
+  int64_t stride_tok, stride_head;  // elements
+  int32_t num_heads;
+  int32_t num_seqs;
+  int64_t total_scale_rows;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_scale;
+  uint8_t* payload;
+  uint8_t* scales;
+};
+
+struct CastParams {
+  const void* x;
+  int x_dtype;
+  int64_t stride_tok, stride_head;
+  int64_t total_tokens;
+  int32_t num_heads;
+  uint8_t* y;
+};
+
+struct AttnParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const void* v;
+  const uint8_t* q_scale;
+  const uint8_t* k_scale;
+  const int32_t* cu_scale_q;
+  const int32_t* cu_scale_k;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  const int32_t* tile_order;
+  uint16_t* out;
+  float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;  // elements
+  int64_t qd_ss, qd_sh, kd_ss, kd_sh, vd_ss, vd_sh;
+  int64_t total_q;
+  int32_t num_heads;
+  int32_t num_seqs;
+  int32_t q_tiles;    // 128-query tiles per (sequence, head) in the default order
+  int32_t num_tiles;  // work tiles to run
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_cast(const CastParams& p, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s);
+
+}  // namespace lpfa

@@ -1,0 +1,153 @@
+// MXFP8 quantizer and unscaled E4M3 cast for packed (tokens, heads, 128) tensors, gfx950.
+//
+// What is computed follows the LP-FA4 README (section "MXFP8 forward and backward"):
+// E4M3 payload, one E8M0 scale per 32-element block along head_dim, per-sequence scale
+// storage padded to 128 tokens, RCEIL default and FLOOR optional. The V cast follows the
+// FastVideo fp8-PV PR (unscaled e4m3 cast of V).
+//
+// Work mapping (HBM-bound, one pass over the input):
+//   16 lanes own one (scale row, head) pair = 128 elements; each lane loads 8 consecutive
+//   elements with one 16-byte load (two for FP32). The 4 lanes of a 32-element block reduce
+//   their maximum with two cross-lane xor steps inside a quad (DPP), derive the exponent from
+//   the maximum's bits, scale by an exact power of two and convert with the hardware E4M3
+//   conversion (round to nearest even). Lane 0 of the 16 gathers the four scale bytes and
+//   writes them as one word. Pad rows of the scale storage get 0x7F and no payload.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace lpfa {
+
+namespace {
+
+// Block exponent from the bits of amax (a non-negative float).
+//   RCEIL: smallest e with amax <= 448 * 2^e. For amax = 1.m * 2^E (normal), 448 = 1.75 * 2^8,
+//          so e = E - 8 if 1.m <= 1.75 (mantissa field <= 0x600000), else E - 7.
+//   FLOOR: e = floor(log2 amax) - 8 = E - 8.
+// Zero or subnormal amax gives an exponent below -127 under both rules: clamp to -127.
+__device__ __forceinline__ int block_exponent(float amax, int mode) {
+  uint32_t bits = __float_as_uint(amax);
+  int biased = (int)(bits >> 23);
+  uint32_t mant = bits & 0x7FFFFFu;
+  int e = biased - 135;
+  if (mode == LPFA_SCALING_RCEIL && mant > 0x600000u) e += 1;
+  if (biased == 0) e = -127;
+  return e < -127 ? -127 : e;  // the largest finite amax gives e = 120, so no upper clamp is hit
+}
+
+template <typename T>
+struct Loader;
+
+template <>
+struct Loader<uint16_t> {  // BF16 bit patterns: 8 elements = one 16-byte load
+  __device__ static void load8(const void* base, int64_t off, float v[8]) {
+    uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+    uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(u[i]);
+      v[2 * i + 1] = bf16_hi(u[i]);
+    }
+  }
+};
+
+template <>
+struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
+  __device__ static void load8(const void* base, int64_t off, float v[8]) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t head_row = gid >> 4;  // (scale row, head) pair
+  const int sub = threadIdx.x & 15;   // 8-element chunk of the 128-element row
+  if (head_row >= p.total_scale_rows * p.num_heads) return;  // all 16 lanes of a row agree
+  const int64_t srow = head_row / p.num_heads;
+  const int h = (int)(head_row - srow * p.num_heads);
+
+  // sequence owning this scale row: the largest i with cu_scale[i] <= srow
+  int lo = 0, hi = p.num_seqs;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if ((int64_t)p.cu_scale[mid] <= srow) lo = mid; else hi = mid;
+  }
+  const int64_t local = srow - p.cu_scale[lo];
+  const int64_t seq_len = (int64_t)p.cu_seqlens[lo + 1] - p.cu_seqlens[lo];
+  uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
+  if (local >= seq_len) {  // pad row of the 128-token-padded scale storage
+    if (sub == 0) *scale_word = 0x7F7F7F7Fu;
+    return;
+  }
+  const int64_t t = p.cu_seqlens[lo] + local;
+
+  float v[8];
+  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // reduce over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the 16)
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = block_exponent(amax, p.scaling_mode);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 120]: normal
+
+  uint32_t w0 = cvt4_e4m3(clamp448(v[0] * inv), clamp448(v[1] * inv), clamp448(v[2] * inv), clamp448(v[3] * inv));
+  uint32_t w1 = cvt4_e4m3(clamp448(v[4] * inv), clamp448(v[5] * inv), clamp448(v[6] * inv), clamp448(v[7] * inv));
+  *reinterpret_cast<uint2*>(p.payload + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
+
+  // gather the 4 block scale bytes of this row into lane 0 of the 16
+  const uint32_t sbyte = (uint32_t)(e + 127);
+  const int base = (threadIdx.x & 63) & ~15;
+  uint32_t b1 = __shfl(sbyte, base + 4);
+  uint32_t b2 = __shfl(sbyte, base + 8);
+  uint32_t b3 = __shfl(sbyte, base + 12);
+  if (sub == 0) *scale_word = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t head_row = gid >> 4;
+  const int sub = threadIdx.x & 15;
+  if (head_row >= p.total_tokens * p.num_heads) return;
+  const int64_t t = head_row / p.num_heads;
+  const int h = (int)(head_row - t * p.num_heads);
+  float v[8];
+  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+  uint32_t w0 = cvt4_e4m3(clamp448(v[0]), clamp448(v[1]), clamp448(v[2]), clamp448(v[3]));
+  uint32_t w1 = cvt4_e4m3(clamp448(v[4]), clamp448(v[5]), clamp448(v[6]), clamp448(v[7]));
+  *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
+  const int64_t threads = p.total_scale_rows * p.num_heads * 16;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.x_dtype == LPFA_DTYPE_BF16)
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const CastParams& p, hipStream_t s) {
+  const int64_t threads = p.total_tokens * p.num_heads * 16;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.x_dtype == LPFA_DTYPE_BF16)
+    hipLaunchKernelGGL(e4m3_cast_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(e4m3_cast_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace lpfa

@@ -1,0 +1,162 @@
+"""GPU parity of the MXFP8 quantizer and the unscaled E4M3 cast: bit-exact against the oracle.
+
+Inputs: an exhaustive sweep of every finite BF16 pattern, laid out in 32-element blocks
+both at their own scale and next to anchors that force other block exponents (so every
+pattern meets RNE ties, subnormal codes and saturation); random FP32 over a wide exponent
+range with subnormals and signed zeros; strided inputs; the workloads' own Q/K, including
+the packed varlen one whose scale storage has pad rows; empty sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_attention_mxfp8_amd as lp
+from synth import make_workload, make_custom, bf16_bits_to_f32
+from helpers import bf16_to_device, f64
+
+pytestmark = pytest.mark.gpu
+
+ANCHORS = [None, 448.0, 1.0, 1.7578125, 2.0 ** 20 * 448, 2.0 ** 100, 3.0e38, 2.0 ** -100, 2.0 ** -126,
+           0.5, 1e-3, 7.0]
+
+
+def _finite_bf16_bits():
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    return bits[np.isfinite(f)].astype(np.uint16)
+
+
+def _sweep_tensor(anchor, rng):
+    """(T, 1, 128) BF16 bits: every finite BF16 pattern once; element 0 of each block is the anchor."""
+    bits = _finite_bf16_bits()
+    rng.shuffle(bits)
+    per = 31 if anchor is not None else 32
+    nblk = -(-len(bits) // per)
+    out = np.zeros((nblk, 32), dtype=np.uint16)
+    flat = np.zeros(nblk * per, dtype=np.uint16)
+    flat[:len(bits)] = bits
+    if anchor is None:
+        out[:] = flat.reshape(nblk, 32)
+    else:
+        a = np.float32(anchor).view(np.uint32) >> 16
+        out[:, 0] = np.where(rng.random(nblk) < 0.5, a, a | 0x8000)
+        out[:, 1:] = flat.reshape(nblk, 31)
+    nblk4 = -(-nblk // 4) * 4
+    full = np.zeros((nblk4, 32), dtype=np.uint16)
+    full[:nblk] = out
+    return full.reshape(-1, 1, 128)
+
+
+def _gpu_quant(x: torch.Tensor, lengths, mode):
+    meta = lp.VarlenMeta.from_lengths(lengths, x.device)
+    mx = lp.quantize_mxfp8_varlen(x, meta, scaling_mode=mode)
+    torch.cuda.synchronize()
+    return mx.payload.cpu().numpy(), mx.scales.cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+@pytest.mark.parametrize("anchor", ANCHORS)
+def test_exhaustive_bf16_sweep(mode, anchor):
+    rng = np.random.default_rng(100 + ANCHORS.index(anchor))
+    bits = _sweep_tensor(anchor, rng)
+    t = bits.shape[0]
+    lengths = [t]
+    x = bf16_to_device(bits)
+    payload, scales = _gpu_quant(x, lengths, mode)
+    rp, rs, _ = oracle.mx_quantize_varlen(f64(bits), np.array([0, t]), mode)
+    assert np.array_equal(scales, rs)
+    bad = np.nonzero(payload != rp)
+    assert bad[0].size == 0, (bad[0][:5], payload[bad][:5], rp[bad][:5], f64(bits)[bad][:5])
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+def test_random_fp32(mode):
+    rng = np.random.default_rng(7)
+    t, h = 300, 3
+    x = rng.standard_normal((t, h, 128)).astype(np.float32)
+    x *= np.exp2(rng.integers(-140, 120, size=(t, h, 4)).repeat(32, axis=2)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] = 0.0
+    x[rng.random(x.shape) < 0.01] = -0.0
+    x[5, 1, :32] = 0.0                                           # an all-zero block
+    x[6, 2, 32:64] = np.float32(1e-42) * np.arange(32)           # subnormal-only block
+    assert np.all(np.isfinite(x))
+    lengths = [100, 0, 77, 123]
+    xg = torch.from_numpy(x).cuda()
+    payload, scales = _gpu_quant(xg, lengths, mode)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    rp, rs, _ = oracle.mx_quantize_varlen(x.astype(np.float64), cu, mode)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(payload, rp)
+
+
+def test_strided_input():
+    """A (T, H, 128) view with token/head strides of a wider buffer (e.g. a fused QKV tensor)."""
+    wl = make_custom([200, 57], [200, 57], heads=4, seed=3)
+    qkv = torch.zeros((257, 3, 4, 128), dtype=torch.bfloat16, device="cuda")
+    qkv[:, 1] = bf16_to_device(wl.q_bits)
+    view = qkv[:, 1]
+    assert view.stride() == (3 * 4 * 128, 128, 1)
+    payload, scales = _gpu_quant(view, [200, 57], "rceil")
+    rp, rs, _ = oracle.mx_quantize_varlen(f64(wl.q_bits), wl.cu_q, "rceil")
+    assert np.array_equal(payload, rp) and np.array_equal(scales, rs)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense", "varlen"])
+def test_workload_qk(name):
+    wl = make_workload(name, seed=0)
+    for bits, lengths in ((wl.q_bits, wl.lengths_q), (wl.k_bits, wl.lengths_k)):
+        payload, scales = _gpu_quant(bf16_to_device(bits), lengths, "rceil")
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        rp, rs, _ = oracle.mx_quantize_varlen(f64(bits), cu, "rceil")
+        assert np.array_equal(payload, rp)
+        assert np.array_equal(scales, rs)   # includes the 0x7F pad rows
+
+
+def test_cross_keys_full_size():
+    """The cross-attention workload's 32768-token key tensor, every byte."""
+    wl = make_workload("cross", seed=0)
+    payload, scales = _gpu_quant(bf16_to_device(wl.k_bits), wl.lengths_k, "rceil")
+    rp, rs, _ = oracle.mx_quantize_varlen(f64(wl.k_bits), wl.cu_k, "rceil")
+    assert np.array_equal(payload, rp) and np.array_equal(scales, rs)
+
+
+def test_empty_and_padding_only():
+    x = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    meta = lp.VarlenMeta.from_lengths([0, 0], "cuda")
+    mx = lp.quantize_mxfp8_varlen(x, meta)
+    assert mx.payload.shape == (0, 2, 128) and mx.scales.shape == (0, 2, 4)
+    x = torch.ones((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    mx = lp.quantize_mxfp8_varlen(x, lp.VarlenMeta.from_lengths([1], "cuda"))
+    torch.cuda.synchronize()
+    s = mx.scales.cpu().numpy()
+    assert s.shape == (128, 2, 4) and np.all(s[0] == 119) and np.all(s[1:] == 0x7F)
+    assert np.all(mx.payload.cpu().numpy() == 0x78)
+
+
+def test_cast_exhaustive_bf16():
+    bits = _finite_bf16_bits()
+    n = -(-len(bits) // 128) * 128
+    full = np.zeros(n, dtype=np.uint16)
+    full[:len(bits)] = bits
+    full = full.reshape(-1, 1, 128)
+    y = lp.cast_e4m3(bf16_to_device(full))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), oracle.e4m3_cast(f64(full)))
+
+
+def test_cast_fp32_and_strided():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((100, 2, 3, 128)) * np.exp2(rng.integers(-20, 12, (100, 2, 3, 1)))).astype(np.float32)
+    xg = torch.from_numpy(x).cuda()[:, 1]                       # strided view (T, 3, 128)
+    y = lp.cast_e4m3(xg)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), oracle.e4m3_cast(x[:, 1].astype(np.float64)))
+
+
+def test_deterministic_repeat():
+    wl = make_workload("dense", seed=1)
+    x = bf16_to_device(wl.q_bits)
+    a = _gpu_quant(x, wl.lengths_q, "rceil")
+    b = _gpu_quant(x, wl.lengths_q, "rceil")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
