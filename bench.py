@@ -7,8 +7,9 @@ benchmark quantizes once and builds metadata up front; here quantization is insi
 and is also reported on its own).
 
 Prints ONE JSON line: value = attention FLOPs (4 * Lq * Lk * H * D summed over sequences)
-per second of whole step; roofline = the attention kernel's own rate from HIP events around
-each of its launches in the timed region, against the dense FP8 matrix peak; cpu_baseline =
+per second of whole step; roofline = the attention kernel's own rate from HIP events that each of its
+dispatches in the timed region stamps at its start and end (hipExtLaunchKernel), against the
+dense FP8 matrix peak; cpu_baseline =
 the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
@@ -53,7 +54,13 @@ def parse():
     ap.add_argument("--pv-mode", default="fp8", choices=["bf16", "fp8"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows per head in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows per (sequence, head) in the oracle sample (default: all of the dense workload)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (reference dispatch "
+                         "for scaling HBM byte counters)")
+    ap.add_argument("--b2b-iters", type=int, default=0,
+                    help="launches in the back-to-back and quantizer-only loops (0: about half a second)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_traffic.json"),
                     help="measured HBM bytes per attention launch (from rocprofv3 counters), if present")
     return ap.parse_args()
@@ -89,33 +96,52 @@ def main():
         pv_mode = "fp8"
     order = lp.longest_first_tile_order(mq, mk, wl.num_heads) if args.workload == "varlen" else None
 
-    # outputs preallocated once; the step writes into them
-    out = torch.empty((mq.total_tokens, wl.num_heads, 128), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((wl.num_heads, mq.total_tokens), dtype=torch.float32, device=dev)
+    # every output (quantized operands, O, LSE) is allocated once; each step writes into it
+    h = wl.num_heads
+    if per_tensor:
+        qx = torch.empty((mq.total_tokens, h, 128), dtype=torch.uint8, device=dev)
+        kx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev)
+    else:
+        qx = lp.Mxfp8Tensor(torch.empty((mq.total_tokens, h, 128), dtype=torch.uint8, device=dev),
+                            torch.empty((mq.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mq)
+        kx = lp.Mxfp8Tensor(torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev),
+                            torch.empty((mk.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mk)
+    vx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev) if pv_mode == "fp8" else v
+    plan = lp.AttnPlan(mq, mk, h, pv_mode=pv_mode, mx=not per_tensor, tile_order=order)
+    out, lse = plan.out, plan.lse
     state = {}
 
     def step():
         if per_tensor:
-            qx, kx = lp.cast_e4m3(q), lp.cast_e4m3(k)
+            lp.cast_e4m3(q, out=qx)
+            lp.cast_e4m3(k, out=kx)
         else:
-            qx = lp.quantize_mxfp8_varlen(q, mq)
-            kx = lp.quantize_mxfp8_varlen(k, mk)
-        vx = lp.cast_e4m3(v) if pv_mode == "fp8" else v
-        state["ops"] = (qx, kx, vx)
-        ev = state.get("ev")
-        if ev is not None:
-            ev[0].record()
-        lp.lp_attn_varlen_fwd(qx, kx, vx, mq, mk, pv_mode=pv_mode, tile_order=order, out=out, lse=lse)
-        if ev is not None:
-            ev[1].record()
+            lp.quantize_mxfp8_varlen(q, mq, out=qx)
+            lp.quantize_mxfp8_varlen(k, mk, out=kx)
+        if pv_mode == "fp8":
+            lp.cast_e4m3(v, out=vx)
+        # in the timed region the kernel's own dispatch stamps a (start, stop) event pair
+        plan(qx, kx, vx, timing=state.get("ev"))
 
     log(f"workload {args.workload} pv_mode {pv_mode}: {flops / 1e9:.2f} GFLOP per forward")
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20)
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)   # one elementwise dispatch: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: one neg dispatch reads {n} bytes and writes {n} bytes")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps; HIP events bracket every attention launch ----
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:   # create the HIP events (torch creates them on first record)
+        e0.record()
+        e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -136,12 +162,11 @@ def main():
         f"median {attn_med_ms * 1e3:.2f} us")
 
     # ---- attention back-to-back (the pages' protocol: quantize once, time the forward) ----
-    qx, kx, vx = state["ops"]
-    n_b2b = max(10, min(2000, int(0.5 / max(attn_avg_ms * 1e-3, 1e-6))))
+    n_b2b = args.b2b_iters or max(10, min(2000, int(0.5 / max(attn_avg_ms * 1e-3, 1e-6))))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(n_b2b):
-        lp.lp_attn_varlen_fwd(qx, kx, vx, mq, mk, pv_mode=pv_mode, tile_order=order, out=out, lse=lse)
+        plan(qx, kx, vx)
     b.record()
     torch.cuda.synchronize()
     b2b_ms = a.elapsed_time(b) / n_b2b
@@ -149,11 +174,11 @@ def main():
     # ---- quantizer alone: Q and K back to back ----
     quant_gbps = None
     if not per_tensor:
-        n_q = 200
+        n_q = args.b2b_iters or 200
         a.record()
         for _ in range(n_q):
-            lp.quantize_mxfp8_varlen(q, mq)
-            lp.quantize_mxfp8_varlen(k, mk)
+            lp.quantize_mxfp8_varlen(q, mq, out=qx)
+            lp.quantize_mxfp8_varlen(k, mk, out=kx)
         b.record()
         torch.cuda.synchronize()
         qms = a.elapsed_time(b) / n_q
@@ -164,9 +189,10 @@ def main():
     # ---- pv bf16 variant of the same workload, for the record ----
     extra = {}
     if not per_tensor and pv_mode == "fp8":
+        plan_bf16 = lp.AttnPlan(mq, mk, h, pv_mode="bf16", tile_order=order, out=out, lse=lse)
         a.record()
         for _ in range(n_b2b):
-            lp.lp_attn_varlen_fwd(qx, kx, v, mq, mk, pv_mode="bf16", tile_order=order, out=out, lse=lse)
+            plan_bf16(qx, kx, v)
         b.record()
         torch.cuda.synchronize()
         bf_ms = a.elapsed_time(b) / n_b2b

@@ -175,6 +175,13 @@ typedef struct lpfa_attn_args {
    * (seq, head, tile) in a default order. Each triple must be listed at most once. */
   const int32_t* tile_order;
   int32_t num_tiles;
+
+  /* Optional timing: hipEvent_t handles the caller created. When set, the attention
+   * kernel's own dispatch records them at its start and end (hipExtLaunchKernel), so
+   * their elapsed time is the kernel's duration with no launch gap. When no kernel is
+   * launched (no query tiles) both are recorded on the stream back to back. */
+  void* start_event;
+  void* stop_event;
 } lpfa_attn_args;
 
 /*

@@ -2,11 +2,11 @@
 
 Public API (marshalling only; the work runs in liblpfa.so):
   VarlenMeta.from_lengths, quantize_mxfp8_varlen, cast_e4m3, lp_attn_varlen_fwd,
-  longest_first_tile_order.
+  AttnPlan (a prepared lp_attn_varlen_fwd for repeated calls), longest_first_tile_order.
 """
-from .api import (Mxfp8Tensor, VarlenMeta, cast_e4m3, longest_first_tile_order, lp_attn_varlen_fwd,
+from .api import (AttnPlan, Mxfp8Tensor, VarlenMeta, cast_e4m3, longest_first_tile_order, lp_attn_varlen_fwd,
                   quantize_mxfp8_varlen)
 from ._lib import LpfaError, load as load_library
 
-__all__ = ["Mxfp8Tensor", "VarlenMeta", "cast_e4m3", "longest_first_tile_order", "lp_attn_varlen_fwd",
+__all__ = ["AttnPlan", "Mxfp8Tensor", "VarlenMeta", "cast_e4m3", "longest_first_tile_order", "lp_attn_varlen_fwd",
            "quantize_mxfp8_varlen", "LpfaError", "load_library"]

@@ -54,6 +54,7 @@ class AttnArgs(ctypes.Structure):
         ("v_descale_stride_seq", _i64), ("v_descale_stride_head", _i64),
         ("out", _p), ("lse", _p),
         ("tile_order", _p), ("num_tiles", _i32),
+        ("start_event", _p), ("stop_event", _p),
     ]
 
 
@@ -72,6 +73,8 @@ class LpfaError(RuntimeError):
 def load() -> ctypes.CDLL:
     """Load liblpfa.so once (raises if it was not built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib

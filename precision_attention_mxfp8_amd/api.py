@@ -103,40 +103,66 @@ def _check_rows(x: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a GPU tensor")
 
 
-def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str = "rceil") -> Mxfp8Tensor:
-    """MXFP8-quantize packed (tokens, heads, 128) BF16/FP32 ``x`` (RCEIL default, FLOOR optional)."""
-    if scaling_mode not in _lib.SCALING:
+def _fp_input(x: torch.Tensor) -> int:
+    _check_rows(x, "x")
+    if x.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if x.dtype == torch.float32:
+        return _lib.DTYPE_FP32
+    raise ValueError("x must be bfloat16 or float32")
+
+
+def _check_out(t: torch.Tensor, shape, dtype, device, name: str) -> None:
+    if t.shape != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device}")
+
+
+def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str = "rceil",
+                          out: Optional[Mxfp8Tensor] = None) -> Mxfp8Tensor:
+    """MXFP8-quantize packed (tokens, heads, 128) BF16/FP32 ``x`` (RCEIL default, FLOOR optional).
+
+    ``out``: an Mxfp8Tensor of the right shapes to write into (reused buffers); a new one otherwise.
+    """
+    mode = _lib.SCALING.get(scaling_mode)
+    if mode is None:
         raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
-    _check_rows(x, "x")
-    if x.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("x must be bfloat16 or float32")
-    if x.shape[0] != meta.total_tokens:
-        raise ValueError(f"x has {x.shape[0]} tokens, metadata says {meta.total_tokens}")
-    lib = _lib.load()
+    dt = _fp_input(x)
     t, h, _ = x.shape
-    payload = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((meta.total_scale_rows, h, 4), dtype=torch.uint8, device=x.device)
-    rc = lib.mxfp8_quantize_varlen(
-        _ptr(x), _lib.DTYPE_BF16 if x.dtype == torch.bfloat16 else _lib.DTYPE_FP32,
-        x.stride(0), x.stride(1), t, h, HEAD_DIM, _ptr(meta.cu_seqlens), _ptr(meta.cu_scale),
-        meta.num_seqs, meta.total_scale_rows, _lib.SCALING[scaling_mode], _ptr(payload), _ptr(scales),
-        _stream())
-    _lib.check("mxfp8_quantize_varlen", rc)
-    return Mxfp8Tensor(payload, scales, meta)
+    if t != meta.total_tokens:
+        raise ValueError(f"x has {t} tokens, metadata says {meta.total_tokens}")
+    if out is None:
+        payload = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((meta.total_scale_rows, h, 4), dtype=torch.uint8, device=x.device)
+        out = Mxfp8Tensor(payload, scales, meta)
+    else:
+        _check_out(out.payload, (t, h, HEAD_DIM), torch.uint8, x.device, "out.payload")
+        _check_out(out.scales, (meta.total_scale_rows, h, 4), torch.uint8, x.device, "out.scales")
+        if out.meta is not meta:
+            out = Mxfp8Tensor(out.payload, out.scales, meta)
+    rc = _lib.load().mxfp8_quantize_varlen(
+        x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM, meta.cu_seqlens.data_ptr(),
+        meta.cu_scale.data_ptr(), meta.num_seqs, meta.total_scale_rows, mode, out.payload.data_ptr(),
+        out.scales.data_ptr(), _stream())
+    if rc:
+        _lib.check("mxfp8_quantize_varlen", rc)
+    return out
 
 
-def cast_e4m3(x: torch.Tensor) -> torch.Tensor:
-    """Unscaled E4M3 cast (fp8 PV mode's V): uint8 codes, same (tokens, heads, 128) shape, contiguous."""
-    _check_rows(x, "x")
-    if x.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("x must be bfloat16 or float32")
-    lib = _lib.load()
+def cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unscaled E4M3 cast (fp8 PV mode's V): uint8 codes, same (tokens, heads, 128) shape, contiguous.
+
+    ``out``: a contiguous uint8 tensor of that shape to write into; a new one otherwise."""
+    dt = _fp_input(x)
     t, h, _ = x.shape
-    y = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
-    rc = lib.lp_fp8_cast_e4m3(_ptr(x), _lib.DTYPE_BF16 if x.dtype == torch.bfloat16 else _lib.DTYPE_FP32,
-                              x.stride(0), x.stride(1), t, h, HEAD_DIM, _ptr(y), _stream())
-    _lib.check("lp_fp8_cast_e4m3", rc)
-    return y
+    if out is None:
+        out = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
+    else:
+        _check_out(out, (t, h, HEAD_DIM), torch.uint8, x.device, "out")
+    rc = _lib.load().lp_fp8_cast_e4m3(x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM,
+                                      out.data_ptr(), _stream())
+    if rc:
+        _lib.check("lp_fp8_cast_e4m3", rc)
+    return out
 
 
 def _as_codes(t: torch.Tensor) -> torch.Tensor:
@@ -182,18 +208,140 @@ def longest_first_tile_order(meta_q: VarlenMeta, meta_k: VarlenMeta, heads: int)
     return torch.tensor(flat, dtype=torch.int32, device=meta_q.device)
 
 
+class AttnPlan:
+    """A prepared attention call: sizes, metadata, scale, descales, work order and outputs are
+    checked and marshalled once; each call then sets the operand pointers and launches.
+
+    Same arguments and semantics as :func:`lp_attn_varlen_fwd`. ``mx`` selects block-scaled
+    QK^T (operands are Mxfp8Tensor) or per-tensor FP8 (operands are raw E4M3 codes). Descale
+    tensors are read at each launch, so they may be updated in place between calls.
+    """
+
+    def __init__(self, meta_q: VarlenMeta, meta_k: VarlenMeta, num_heads: int, pv_mode: str = "bf16",
+                 mx: bool = True, softmax_scale: Optional[float] = None, q_descale: Descale = None,
+                 k_descale: Descale = None, v_descale: Descale = None,
+                 tile_order: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None):
+        if pv_mode not in _lib.PV_MODES:
+            raise ValueError(f"pv_mode must be one of {sorted(_lib.PV_MODES)}, got {pv_mode!r}")
+        if meta_q.num_seqs != meta_k.num_seqs:
+            raise ValueError("query and key metadata have different sequence counts")
+        for lq, lk in zip(meta_q.lengths, meta_k.lengths):
+            if lq > 0 and lk == 0:
+                raise ValueError("a sequence with queries must have at least one key")
+        if meta_q.device != meta_k.device or meta_q.device.type != "cuda":
+            raise ValueError("metadata must live on one GPU")
+        h = int(num_heads)
+        if h < 1:
+            raise ValueError("num_heads must be positive")
+        dev = meta_q.device
+        tq, tk = meta_q.total_tokens, meta_k.total_tokens
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+        if out is None:
+            out = torch.empty((tq, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((h, tq), dtype=torch.float32, device=dev)
+        if out.shape != (tq, h, HEAD_DIM) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bfloat16 (Tq, H, 128) tensor")
+        if lse.shape != (h, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 (H, Tq) tensor")
+        qd, qss, qsh = _descale(q_descale, meta_q.num_seqs, h, dev)
+        kd, kss, ksh = _descale(k_descale, meta_q.num_seqs, h, dev)
+        vd, vss, vsh = _descale(v_descale, meta_q.num_seqs, h, dev)
+
+        a = _lib.AttnArgs()
+        a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+        a.pv_mode = _lib.PV_MODES[pv_mode]
+        if mx:
+            a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
+        a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
+        a.num_seqs = meta_q.num_seqs
+        a.max_seqlen_q, a.max_seqlen_k = meta_q.max_seqlen, meta_k.max_seqlen
+        a.total_q, a.total_k = tq, tk
+        a.num_heads, a.head_dim = h, HEAD_DIM
+        a.softmax_scale = float(softmax_scale)
+        a.causal = 0
+        a.q_descale, a.k_descale, a.v_descale = _ptr(qd), _ptr(kd), _ptr(vd)
+        a.q_descale_stride_seq, a.q_descale_stride_head = qss, qsh
+        a.k_descale_stride_seq, a.k_descale_stride_head = kss, ksh
+        a.v_descale_stride_seq, a.v_descale_stride_head = vss, vsh
+        a.out, a.lse = _ptr(out), _ptr(lse)
+        if tile_order is not None:
+            if tile_order.dtype != torch.int32 or not tile_order.is_cuda or tile_order.numel() % 3:
+                raise ValueError("tile_order must be a GPU int32 tensor of (seq, head, tile) triples")
+            a.tile_order, a.num_tiles = _ptr(tile_order), tile_order.numel() // 3
+        self._args = a
+        self._ref = ctypes.byref(a)
+        self._keep = (meta_q, meta_k, qd, kd, vd, tile_order)   # everything the struct points at
+        self._fn = _lib.load().lp_attn_varlen_fwd
+        self.meta_q, self.meta_k, self.num_heads, self.mx, self.pv_mode = meta_q, meta_k, h, bool(mx), pv_mode
+        self.out, self.lse = out, lse
+        self._qshape, self._kshape = (tq, h, HEAD_DIM), (tk, h, HEAD_DIM)
+        self._vdtype = torch.bfloat16 if pv_mode == "bf16" else torch.uint8
+        self._dev = out.device                    # indexed ("cuda:0"), as operand tensors report it
+
+    def _operand(self, t: torch.Tensor, shape, dtype, name: str) -> None:
+        if t.dtype == torch.float8_e4m3fn and dtype == torch.uint8:
+            t = t.view(torch.uint8)
+        if t.shape != shape or t.dtype != dtype or t.stride(2) != 1 or t.device != self._dev:
+            raise ValueError(f"{name} must be a {dtype} tensor of shape {shape} on {self._dev}, contiguous "
+                             f"along head_dim (got {t.dtype} {tuple(t.shape)} on {t.device})")
+
+    def __call__(self, q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor, torch.Tensor],
+                 v: torch.Tensor, timing: Optional[Tuple] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        a = self._args
+        if self.mx:
+            if not (isinstance(q, Mxfp8Tensor) and isinstance(k, Mxfp8Tensor)):
+                raise ValueError("this plan is block-scaled: q and k must be Mxfp8Tensor")
+            if (q.meta is not self.meta_q and q.meta.cu_scale_host != self.meta_q.cu_scale_host) or \
+                    (k.meta is not self.meta_k and k.meta.cu_scale_host != self.meta_k.cu_scale_host):
+                raise ValueError("q/k were quantized with different sequence metadata")
+            qp, kp = q.payload, k.payload
+            a.q_scale, a.k_scale = q.scales.data_ptr(), k.scales.data_ptr()
+            if q.scales.shape != (self.meta_q.total_scale_rows, self.num_heads, 4) or \
+                    k.scales.shape != (self.meta_k.total_scale_rows, self.num_heads, 4):
+                raise ValueError("scale tensors do not match the metadata")
+        else:
+            if isinstance(q, Mxfp8Tensor) or isinstance(k, Mxfp8Tensor):
+                raise ValueError("this plan is per-tensor FP8: q and k must be raw E4M3 codes")
+            qp, kp = q, k
+        self._operand(qp, self._qshape, torch.uint8, "q")
+        self._operand(kp, self._kshape, torch.uint8, "k")
+        self._operand(v, self._kshape, self._vdtype, "v")
+        a.q, a.k, a.v = qp.data_ptr(), kp.data_ptr(), v.data_ptr()
+        a.q_stride_tok, a.q_stride_head = qp.stride(0), qp.stride(1)
+        a.k_stride_tok, a.k_stride_head = kp.stride(0), kp.stride(1)
+        a.v_stride_tok, a.v_stride_head = v.stride(0), v.stride(1)
+        if timing is not None:
+            st, sp = (int(getattr(e, "cuda_event", e) or 0) for e in timing)
+            if not st or not sp:
+                raise ValueError("timing events must exist: record each once before passing them")
+            a.start_event, a.stop_event = st, sp
+        else:
+            a.start_event = a.stop_event = None
+        rc = self._fn(self._ref, _stream())
+        if rc:
+            _lib.check("lp_attn_varlen_fwd", rc)
+        return self.out, self.lse
+
+
 def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor, torch.Tensor],
                        v: torch.Tensor, meta_q: VarlenMeta, meta_k: VarlenMeta, pv_mode: str = "bf16",
                        softmax_scale: Optional[float] = None, q_descale: Descale = None,
                        k_descale: Descale = None, v_descale: Descale = None,
                        tile_order: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       lse: Optional[torch.Tensor] = None,
+                       timing: Optional[Tuple] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Noncausal head_dim-128 attention forward over packed sequences -> (out BF16 (Tq,H,128), lse FP32 (H,Tq)).
 
     ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T) or raw E4M3 codes (per-tensor FP8 mode).
     ``v`` is BF16 for ``pv_mode="bf16"`` or E4M3 codes for ``pv_mode="fp8"`` (unscaled, see
     :func:`cast_e4m3`). Descales are floats or fp32 tensors broadcastable to (num_seqs, heads).
+    ``timing``: optional (start, stop) ``torch.cuda.Event`` pair with timing enabled, each
+    recorded once before (so the handles exist); the kernel's dispatch stamps them, and
+    ``start.elapsed_time(stop)`` is then the kernel's own duration.
     """
     if pv_mode not in _lib.PV_MODES:
         raise ValueError(f"pv_mode must be one of {sorted(_lib.PV_MODES)}, got {pv_mode!r}")
@@ -202,67 +350,18 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
         raise ValueError("q and k must both be Mxfp8Tensor (MX mode) or both raw E4M3 (per-tensor mode)")
     qp = q.payload if mx_q else _as_codes(q)
     kp = k.payload if mx_k else _as_codes(k)
-    _check_rows(qp, "q")
-    _check_rows(kp, "k")
-    _check_rows(v, "v")
+    for t, name in ((qp, "q"), (kp, "k"), (v, "v")):
+        _check_rows(t, name)
     if pv_mode == "bf16" and v.dtype != torch.bfloat16:
         raise ValueError("pv_mode='bf16' needs a bfloat16 V")
     if pv_mode == "fp8":
         v = _as_codes(v)
-    if meta_q.num_seqs != meta_k.num_seqs:
-        raise ValueError("query and key metadata have different sequence counts")
-    for lq, lk in zip(meta_q.lengths, meta_k.lengths):
-        if lq > 0 and lk == 0:
-            raise ValueError("a sequence with queries must have at least one key")
-    tq, h, _ = qp.shape
-    tk = kp.shape[0]
-    if tq != meta_q.total_tokens or tk != meta_k.total_tokens or v.shape[0] != tk:
+    if qp.shape[0] != meta_q.total_tokens or kp.shape[0] != meta_k.total_tokens or v.shape[0] != kp.shape[0]:
         raise ValueError("tensor token counts do not match the metadata")
+    h = qp.shape[1]
     if kp.shape[1] != h or v.shape[1] != h:
         raise ValueError("q, k and v must have the same number of heads")
-    if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
-    dev = qp.device
-    if out is None:
-        out = torch.empty((tq, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((h, tq), dtype=torch.float32, device=dev)
-    if out.shape != (tq, h, HEAD_DIM) or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 (Tq, H, 128) tensor")
-    if lse.shape != (h, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 (H, Tq) tensor")
-
-    qd, qss, qsh = _descale(q_descale, meta_q.num_seqs, h, dev)
-    kd, kss, ksh = _descale(k_descale, meta_q.num_seqs, h, dev)
-    vd, vss, vsh = _descale(v_descale, meta_q.num_seqs, h, dev)
-
-    a = _lib.AttnArgs()
-    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
-    a.q, a.k = _ptr(qp), _ptr(kp)
-    a.q_stride_tok, a.q_stride_head = qp.stride(0), qp.stride(1)
-    a.k_stride_tok, a.k_stride_head = kp.stride(0), kp.stride(1)
-    if mx_q:
-        a.q_scale, a.k_scale = _ptr(q.scales), _ptr(k.scales)
-        a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
-    a.v = _ptr(v)
-    a.v_stride_tok, a.v_stride_head = v.stride(0), v.stride(1)
-    a.pv_mode = _lib.PV_MODES[pv_mode]
-    a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
-    a.num_seqs = meta_q.num_seqs
-    a.max_seqlen_q, a.max_seqlen_k = meta_q.max_seqlen, meta_k.max_seqlen
-    a.total_q, a.total_k = tq, tk
-    a.num_heads, a.head_dim = h, HEAD_DIM
-    a.softmax_scale = float(softmax_scale)
-    a.causal = 0
-    a.q_descale, a.k_descale, a.v_descale = _ptr(qd), _ptr(kd), _ptr(vd)
-    a.q_descale_stride_seq, a.q_descale_stride_head = qss, qsh
-    a.k_descale_stride_seq, a.k_descale_stride_head = kss, ksh
-    a.v_descale_stride_seq, a.v_descale_stride_head = vss, vsh
-    a.out, a.lse = _ptr(out), _ptr(lse)
-    if tile_order is not None:
-        if tile_order.dtype != torch.int32 or not tile_order.is_cuda or tile_order.numel() % 3:
-            raise ValueError("tile_order must be a GPU int32 tensor of (seq, head, tile) triples")
-        a.tile_order, a.num_tiles = _ptr(tile_order), tile_order.numel() // 3
-    rc = _lib.load().lp_attn_varlen_fwd(ctypes.byref(a), _stream())
-    _lib.check("lp_attn_varlen_fwd", rc)
-    return out, lse
+    plan = AttnPlan(meta_q, meta_k, h, pv_mode=pv_mode, mx=mx_q, softmax_scale=softmax_scale,
+                    q_descale=q_descale, k_descale=k_descale, v_descale=v_descale, tile_order=tile_order,
+                    out=out, lse=lse)
+    return plan(q if mx_q else qp, k if mx_k else kp, v, timing=timing)

@@ -101,7 +101,9 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   p.q_tiles = (a->max_seqlen_q + 127) / 128;
   p.num_tiles = a->tile_order ? a->num_tiles : a->num_seqs * a->num_heads * p.q_tiles;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
-  return launch_status(lpfa::launch_attention(p, a->q_scale != nullptr, a->pv_mode, static_cast<hipStream_t>(stream)),
+  return launch_status(lpfa::launch_attention(p, a->q_scale != nullptr, a->pv_mode, static_cast<hipStream_t>(stream),
+                                               static_cast<hipEvent_t>(a->start_event),
+                                               static_cast<hipEvent_t>(a->stop_event)),
                        "attention");
 }
 

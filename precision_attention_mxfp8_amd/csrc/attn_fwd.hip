@@ -54,7 +54,10 @@
 // Workgroup ids are remapped so that consecutive tiles of one (sequence, head) land on the same
 // XCD (ids are dealt round-robin over the 8 XCDs), sharing K/V in that XCD's L2.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -643,30 +646,49 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
 }
 
 template <bool MX, bool FP8V>
-hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s) {
-  static bool configured = false;  // raising the dynamic LDS limit is per kernel, once
+hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  // Raising the dynamic LDS limit is a per-kernel, per-device attribute: done once per device.
+  static std::atomic<uint64_t> configured{0};
   const int bytes = Lay<FP8V>::TOTAL;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V>), grid, dim3(256), bytes, s, p);
-  return hipGetLastError();
+  if (start == nullptr && stop == nullptr) {
+    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V>), grid, dim3(256), bytes, s, p);
+    return hipGetLastError();
+  }
+  // The dispatch itself stamps the events: their interval is the kernel, without launch gaps.
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>), grid, dim3(256), args,
+                            bytes, s, start, stop, 0);
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s) {
-  if (p.num_tiles == 0) return hipSuccess;
+hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s, hipEvent_t start,
+                            hipEvent_t stop) {
+  if (p.num_tiles == 0) {
+    if (start) {
+      hipError_t e = hipEventRecord(start, s);
+      if (e != hipSuccess) return e;
+    }
+    return stop ? hipEventRecord(stop, s) : hipSuccess;
+  }
   unsigned grid = (unsigned)p.num_tiles;
   if (p.tile_order == nullptr) grid = (grid + 7u) & ~7u;  // XCD remap needs a multiple of 8
   const bool fp8v = pv_mode == LPFA_PV_FP8;
-  if (mx && fp8v) return launch_variant<true, true>(p, dim3(grid), s);
-  if (mx) return launch_variant<true, false>(p, dim3(grid), s);
-  if (fp8v) return launch_variant<false, true>(p, dim3(grid), s);
-  return launch_variant<false, false>(p, dim3(grid), s);
+  if (mx && fp8v) return launch_variant<true, true>(p, dim3(grid), s, start, stop);
+  if (mx) return launch_variant<true, false>(p, dim3(grid), s, start, stop);
+  if (fp8v) return launch_variant<false, true>(p, dim3(grid), s, start, stop);
+  return launch_variant<false, false>(p, dim3(grid), s, start, stop);
 }
 
 }  // namespace lpfa

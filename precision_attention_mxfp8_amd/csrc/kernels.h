@@ -58,6 +58,7 @@ struct AttnParams {
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_cast(const CastParams& p, hipStream_t s);
-hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
+                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace lpfa

@@ -129,11 +129,12 @@ def test_varlen_sampled(tile_order):
                                   rows=_rows(wl, 13))
     st = compare(out, lse, ref)
     assert_within(st, bf16_allowance=True)
-    # the allowance is only ever needed where the output itself is large
+    # the allowance is only ever needed where the output itself is large: at |O| >= 2 one BF16
+    # ulp (2^-6 or more) is already most of the absolute bound
     o = out.float().cpu().numpy().astype(np.float64)
     mask = ~np.isnan(ref.lse[0])
     big_err = np.abs(o[mask] - ref.out[mask]) > 2e-2
-    assert np.all(np.abs(ref.out[mask][big_err]) >= 4.0)
+    assert np.all(np.abs(ref.out[mask][big_err]) >= 2.0)
 
 
 @pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
@@ -278,3 +279,56 @@ def test_deterministic_and_tile_order_invariant():
     o3, l3, _, _ = _run_mx(wl, "fp8", tile_order=True)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+
+
+def test_timing_events_stamped_by_dispatch():
+    """Events passed in the args are recorded by the kernel's own dispatch: the output is the same
+    as without them, and their interval is positive and no longer than events recorded around
+    the launch on the stream."""
+    wl = make_custom([1000, 700], [900, 1200], heads=4, seed=71)
+    ref_o, ref_l, _, _ = _run_mx(wl, "fp8")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in (e0, e1):
+        e.record()
+    torch.cuda.synchronize()
+    b0.record()
+    out, lse, _, _ = _run_mx(wl, "fp8", timing=(e0, e1))
+    b1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(lse, ref_l)
+    kernel_ms, bracket_ms = e0.elapsed_time(e1), b0.elapsed_time(b1)
+    assert 0.0 < kernel_ms <= bracket_ms
+    with pytest.raises(ValueError):
+        _run_mx(wl, "fp8", timing=(0, 0))
+
+
+@pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
+def test_plan_and_reused_buffers_match_functional(pv_mode):
+    """AttnPlan and the out= quantizer buffers give the functional API's bits, call after call,
+    and a plan refuses operands that do not match what it was prepared for."""
+    dev = torch.device("cuda")
+    wl1 = make_custom([300, 77], [260, 500], heads=3, seed=81)
+    wl2 = make_custom([300, 77], [260, 500], heads=3, seed=82)
+    mq = lp.VarlenMeta.from_lengths(wl1.lengths_q, dev)
+    mk = lp.VarlenMeta.from_lengths(wl1.lengths_k, dev)
+    plan = lp.AttnPlan(mq, mk, 3, pv_mode=pv_mode)
+    qx = lp.quantize_mxfp8_varlen(bf16_to_device(wl2.q_bits), mq)     # buffers reused below
+    kx = lp.quantize_mxfp8_varlen(bf16_to_device(wl2.k_bits), mk)
+    vx = torch.empty((mk.total_tokens, 3, 128), dtype=torch.uint8, device=dev)
+    for wl in (wl1, wl2, wl1):
+        ref_o, ref_l, _, _ = _run_mx(wl, pv_mode)
+        lp.quantize_mxfp8_varlen(bf16_to_device(wl.q_bits), mq, out=qx)
+        lp.quantize_mxfp8_varlen(bf16_to_device(wl.k_bits), mk, out=kx)
+        v = bf16_to_device(wl.v_bits)
+        if pv_mode == "fp8":
+            v = lp.cast_e4m3(v, out=vx)
+        o, l = plan(qx, kx, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(l, ref_l)
+    with pytest.raises(ValueError):
+        plan(qx.payload, kx.payload, v)                   # raw codes into a block-scaled plan
+    with pytest.raises(ValueError):
+        plan(kx, qx, v)                                   # shapes swapped (Lq != Lk)
+    with pytest.raises(ValueError):
+        lp.cast_e4m3(bf16_to_device(wl1.v_bits), out=torch.empty((1, 3, 128), dtype=torch.uint8, device=dev))
