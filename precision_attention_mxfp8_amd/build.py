@@ -27,6 +27,10 @@ def build_command(output: str = OUTPUT):
             # matrix-instruction results in VGPRs: the softmax reads the score tiles with VALU ops,
             # and AGPR results would cost one v_accvgpr_read per element.
             "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            # keep matrix instructions where they are written: sinking them toward their uses
+            # (past the attention loop's load-issue code) keeps every operand fragment alive at
+            # once and spills the two-group loop
+            "-mllvm", "-disable-machine-sink",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", output] + \
            [os.path.join(CSRC, s) for s in SOURCES]
 

@@ -95,6 +95,14 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   p.kd_sh = a->k_descale_stride_head;
   p.vd_ss = a->v_descale_stride_seq;
   p.vd_sh = a->v_descale_stride_head;
+  {
+    // one past the last byte of the K and V tensors (the kernel's loads are range-checked)
+    const int64_t vb = a->pv_mode == LPFA_PV_FP8 ? 1 : 2;
+    const int64_t kspan = a->total_k > 0 ? (a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128 : 0;
+    const int64_t vspan = a->total_k > 0 ? ((a->total_k - 1) * a->v_stride_tok + (int64_t)(a->num_heads - 1) * a->v_stride_head + 128) * vb : 0;
+    p.k_end = a->k + kspan;
+    p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
+  }
   p.total_q = a->total_q;
   p.num_heads = a->num_heads;
   p.num_seqs = a->num_seqs;

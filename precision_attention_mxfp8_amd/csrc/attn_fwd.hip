@@ -5,8 +5,11 @@
 // cast read with dequant scale 1.0, output BF16; vLLM unit-descale PR: optional per-tensor
 // descales, a missing one read as 1.0 through the same arithmetic.
 //
-// Work split: one workgroup = one (sequence, head, 128-query tile); 4 waves x 32 queries, one
-// wave per SIMD. Keys are processed in blocks of 128.
+// Work split: one workgroup = one (sequence, head, 128-query tile). A wave group is 4 waves x
+// 32 queries. With E4M3 V the workgroup has two wave groups that take alternate 128-key
+// blocks (group 0 the even ones, group 1 the odd ones) and merge their partial (m, l, O) at
+// the end; each SIMD then holds two waves, so the matrix work and waits of one overlap the
+// softmax of the other. BF16 V tiles are twice as large: one group (LDS would not hold two).
 //
 // Matrix instructions and register layouts
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_scale_f32_16x16x128_f8f6f4: one
@@ -31,25 +34,29 @@
 //      K row r: 16-byte chunk c stored at c ^ (r & 7)          (conflict-free score operand reads)
 //      V fp8 row r: chunk c stored at c ^ ((r & 3) | ((r >> 2) & 4))   (conflict-free tr_b8 reads)
 //      V bf16 row r: chunk c stored at c ^ (2 * (r & 3))             (conflict-free tr_b16 reads)
-//  * K is double-buffered and V triple-buffered so that the loads for blocks j+2 (K) and j+1 (V)
-//    are issued a full iteration before they are needed.
+//    The per-lane part of every load address is fixed for the whole sequence; each block only
+//    moves a uniform base. Only a sequence's last, partial block clamps rows to the last key.
+//  * Each group double-buffers K and V: in its local iteration j it loads K for its block j+2
+//    and V for its block j, and waits for both at the end of the iteration.
 //
-// Pipeline (iteration j): the score instructions for block j+1 and the P V instructions for
-// block j-1 overlap the softmax VALU work of block j. In the BF16 mode the running maximum is
-// lazy (see Lazy) and O is normalised by the sum of the probabilities as rounded for the P V
-// instruction (summed on the matrix core against an all-ones tile), so a dominant probability's
-// rounding cancels; in the FP8 mode the maximum is exact and O uses the FP32 sum. LSE always
-// uses the unrounded FP32 sum.
+// Pipeline (local iteration j): the score instructions for block j+1 and the P V instructions
+// for block j-1 overlap the softmax VALU work of block j. The running maximum is lazy: it only
+// moves when a row's maximum exceeds it by more than 2^8, so the probabilities stay <= 256
+// (inside E4M3 and BF16 range) and O is rarely rescaled. O is normalised by the sum of the
+// probabilities as rounded for the P V instruction (summed on the matrix core against an
+// all-ones tile), so a dominant probability's rounding cancels; LSE uses the unrounded FP32
+// sum. The loop is unrolled twice so that the probability fragments of consecutive blocks
+// alternate between two register sets without copies.
 //
 // Precision guard: the FP8 matrix instructions sum each group of 8 consecutive products on a
 // fixed-point grid 13 bits below the group's largest product (truncating) and the groups in
 // FP32, so a score carries an absolute error up to ~2^-12 of the largest product in its row.
-// Before each key block the kernel bounds c * max|q| * max|k| (c = softmax_scale * log2 e *
+// Before the key loop the workgroup bounds c * max|q| * max|k| (c = softmax_scale * log2 e *
 // descales; in MX mode from the E8M0 scales: block maxima lie in (224, 448] * 2^e; in
-// per-tensor mode from the E4M3 range 448). Above GUARD_LOG2 = 16 the block's scores are
-// computed instead with v_mfma_f32_16x16x32_bf16 on exactly dequantized operands
-// (v_cvt_scalef32_pk_bf16_fp8), whose accumulation is FP32-exact in practice. Typical N(0,1)
-// data stays on the FP8 path; rows dominated by outliers take the BF16 path.
+// per-tensor mode from the E4M3 codes of Q and the E4M3 range 448 for K). Above GUARD_LOG2 = 16
+// the scores are computed instead with v_mfma_f32_16x16x32_bf16 on exactly dequantized
+// operands (v_cvt_scalef32_pk_bf16_fp8), whose accumulation is FP32-exact in practice. Typical
+// N(0,1) data stays on the FP8 path; tiles whose rows meet outliers take the BF16 path.
 //
 // Workgroup ids are remapped so that consecutive tiles of one (sequence, head) land on the same
 // XCD (ids are dealt round-robin over the 8 XCDs), sharing K/V in that XCD's L2.
@@ -70,45 +77,56 @@ constexpr int BM = 128;  // queries per workgroup
 constexpr int BN = 128;  // keys per block
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float GUARD_LOG2 = 16.0f;
-// Stale-maximum slack of the online softmax, in log2 units. BF16 probabilities may be taken
-// against a maximum up to 8 below the running one (P <= 2^8); E4M3 probabilities are rounded
-// against the exact running maximum, so that the largest probability is exactly 1 and the
-// rounding of the others tracks a rounding against the final maximum as closely as a single
-// pass allows (a stale maximum shifts every probability by a non-power-of-two factor and
-// decorrelates the E4M3 rounding).
-template <bool FP8V>
-struct Lazy { static constexpr float LOG2 = FP8V ? 0.0f : 8.0f; };
+// Stale-maximum slack of the online softmax, in log2 units: probabilities may be taken against
+// a maximum up to 8 below the running one (P <= 2^8).
+constexpr float LAZY_LOG2 = 8.0f;
 
-typedef int v2i_t __attribute__((ext_vector_type(2)));
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
-typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
-// BF16 operands are always assembled from whole 32-bit words: building them element by element
-// from 16-bit values lets the compiler repack halves (it has emitted a repack that dropped the
-// second register of a transposed read).
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-#define LDS __attribute__((address_space(3)))
-// LDS byte address (32-bit) -> typed LDS pointer, so offsets fold into the DS immediate field.
-template <typename T>
-__device__ __forceinline__ LDS T* lds_at(uint32_t byte_addr) {
-  return reinterpret_cast<LDS T*>(static_cast<uintptr_t>(byte_addr));
-}
+template <bool FP8V>
+struct Groups { static constexpr int G = FP8V ? 2 : 1; };
 
 template <bool FP8V>
 struct Lay {
   static constexpr int K_BYTES = BN * 128;
   static constexpr int KSC_BYTES = BN * 4;
   static constexpr int V_BYTES = FP8V ? BN * 128 : BN * 256;
-  static constexpr int OFF_K = 0;                       // 2 buffers
-  static constexpr int OFF_KSC = 2 * K_BYTES;           // 2 buffers
-  static constexpr int OFF_V = OFF_KSC + 2 * KSC_BYTES; // 3 buffers
-  static constexpr int TOTAL = OFF_V + 3 * V_BYTES + 16;  // + guard reduction slots
+  // Dynamic LDS: K and its scales (read with ordinary LDS loads).
+  static constexpr int OFF_K = 0;                        // 2 buffers
+  static constexpr int OFF_KSC = 2 * K_BYTES;            // 2 buffers
+  static constexpr int GROUP_BYTES = OFF_KSC + 2 * KSC_BYTES;
+  static constexpr int OFF_RED = Groups<FP8V>::G * GROUP_BYTES;  // guard reduction slots
+  // Q fragments (score B operands) of the 4 query waves: per (wave, 16-query tile) two 1 KB
+  // halves, lane L's 16-byte pieces at L * 16 (conflict-free 16-byte reads). Reloaded for
+  // each score phase instead of held in registers.
+  static constexpr int OFF_Q = OFF_RED + 64;
+  static constexpr int TOTAL = OFF_Q + 4 * 2 * 2048;
+  // V buffers live in two static LDS objects of 32 KB, apart from the dynamic K area, so loads
+  // in flight into K never hold up the transposing V reads (the compiler makes those reads wait
+  // for every outstanding load into the same object). One group: object i is V buffer i. Two
+  // groups: object g holds group g's two V buffers, and each group issues its V loads only
+  // after its own V reads of the iteration. The merge of the two groups reuses the objects
+  // (16 v4f per lane per wave of group 1) plus 2 v4f per lane per wave of the K area.
+  static constexpr int VOBJ_BYTES = 32768;
+  static_assert(V_BYTES * Groups<FP8V>::G == VOBJ_BYTES, "V objects");
+  static_assert(Groups<FP8V>::G == 1 || (16 * 64 * 16 <= VOBJ_BYTES / 2 && 4 * 2 * 64 * 16 <= OFF_RED), "merge area");
 };
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+// BF16 operands are always assembled from whole 32-bit words: building them element by element
+// from 16-bit values lets the compiler repack halves (it has emitted a repack that dropped the
+// second register of a transposed read).
+#define LDS __attribute__((address_space(3)))
+#define LDS_PTR(T, p) ((LDS T*)(p))
+// LDS byte address (32-bit) -> typed LDS pointer, so offsets fold into the DS immediate field.
+template <typename T>
+__device__ __forceinline__ LDS T* lds_at(uint32_t byte_addr) {
+  return reinterpret_cast<LDS T*>(static_cast<uintptr_t>(byte_addr));
+}
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ldg8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
-
-typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v8i make_v8i(v4u_t a, v4u_t b) {
   v8i r;
@@ -138,37 +156,64 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1, float sc
 // scaled conversion reads as 2^-127).
 __device__ __forceinline__ float e8m0_to_float(uint32_t b) { return __uint_as_float(b << 23); }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
-  return x;
-}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, s));
   return x;
 }
 
+// max over lanes i, i^16, i^32, i^48 (the 4 lane groups holding one query row) with the
+// gfx950 lane-swap instructions: with both operands equal, the 16-swap pairs row r with r^1 and
+// the 32-swap pairs the two halves.
+__device__ __forceinline__ float xmax16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Ends a scheduling region: no instruction is moved across it, and (compiler-only memory
+// fence, no instruction emitted) no memory access either, so LDS operand reads stay with
+// the matrix instructions that use them instead of all being hoisted ahead.
+__device__ __forceinline__ void region_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Probability fragments of one key block (B operand of the P V instructions).
+//   fp8 mode:  one v8i per 16-query tile; byte 4*mt + i = key 16*mt + 4*g + i.
+//   bf16 mode: per 32-key chunk u and query tile, 4 words; element j = key 32u + 16*(j/4) + 4*g + j%4.
+template <bool FP8V>
+struct PFrag;
+template <>
+struct PFrag<true> { v8i f8[2]; };
+template <>
+struct PFrag<false> { uint32_t w[4][2][4]; };
 
 template <bool MX, bool FP8V>
 struct Attn {
   using L = Lay<FP8V>;
+  using PF = PFrag<FP8V>;
+  static constexpr int G = Groups<FP8V>::G;
 
   // ---- per-workgroup constants ----
   const AttnParams& p;
-  uint8_t* lds;
-  uint32_t lds_base;         // LDS byte address of the dynamic allocation
+  uint8_t* lds;              // this wave group's K buffers (dynamic LDS)
+  uint32_t lds_base;         // the same, as an LDS byte address
+  LDS uint8_t* vobj[2];      // the two static V objects; always indexed by constants
   int seq, head, H, Lk, nb;
-  int lane, wave, n16, g;
+  int lane, wave, n16, g;    // wave: index inside the group (queries 32*wave ..)
+  int grp, ng;               // wave group, and the number of key blocks it processes
   const uint8_t* kbase;      // key row 0 of this (sequence, head)
   const uint8_t* vbase;      // value row 0 (bytes)
   int64_t k_st_b, v_st_b;    // row strides in bytes
   const uint8_t* ksc_base;   // scale word of key row 0 of this (sequence, head)
   float c;                   // softmax_scale * log2(e) * qd * kd
 
+
   // ---- per-wave state ----
-  v8i qf[2];
   int qsc[2];
   float qbound;              // max |q| bound of the wave's queries
   const uint8_t* qrow[2];    // this lane's query rows (nullptr past the end)
@@ -177,60 +222,81 @@ struct Attn {
   v4f o[8][2];
   v4f o_sum[2];              // sum over keys of the rounded probabilities (ones tile of V^T)
 
-  __device__ Attn(const AttnParams& p_, uint8_t* lds_)
-      : p(p_), lds(lds_), lds_base((uint32_t)(uintptr_t)(LDS uint8_t*)lds_) {}
+  __device__ Attn(const AttnParams& p_, uint8_t* lds_, int grp_, LDS uint8_t* va, LDS uint8_t* vb)
+      : p(p_), lds(lds_ + grp_ * L::GROUP_BYTES),
+        lds_base((uint32_t)(uintptr_t)(LDS uint8_t*)lds_ + grp_ * L::GROUP_BYTES), grp(grp_) {
+    vobj[0] = va;
+    vobj[1] = vb;
+  }
+
+  // key block processed by this group in its local iteration i
+  __device__ __forceinline__ int blk(int i) const { return G * i + grp; }
 
   // ---------------------------------------------------------------- global -> LDS
-  // Per-lane byte offsets of the rows each lane fetches, relative to the block's first row
-  // (uniform base, so the loads use the scalar-base addressing form). Rows past the end of
-  // the sequence are clamped to its last row (those keys are masked, their V rows get P = 0).
-  __device__ __forceinline__ uint32_t k_lane_off(int i, int kb, bool clamp) const {
-    const int r = 8 * (4 * wave + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (lane >> 3);
-    const int row = clamp ? min(r, Lk - 1 - kb) : r;
-    return (uint32_t)(row * (int)k_st_b) + 16u * c;
+  // Buffer loads straight to LDS: the block's base (uniform) goes into a buffer descriptor
+  // whose range ends at the tensor's last byte, so rows past the end of the last sequence
+  // read zeros (rows past a sequence's end inside the tensor are other sequences' keys: masked
+  // scores, zero probabilities). Each lane's 32-bit offsets are fixed for the whole sequence.
+  // K: instruction i of wave w fills 1 KB region R = 4w + i = key rows 8R..8R+7; lane L fetches
+  // row 8R + L/8, chunk (L%8) ^ (L/8). V fp8: same rows, chunk (L%8) ^ ((L/8)%4 | 4*(i/2)). V bf16:
+  // region R = 8w + i = rows 4R..4R+3 of 256 B; lane L fetches row 4R + L/16, chunk (L%16) ^ 2((L/16)%4).
+  // K scales: waves 0 and 1 fetch 64 rows each, one 4-byte word per lane (the scale storage is
+  // padded to whole blocks, so every row exists).
+  // The row step between a wave's instructions goes into a descriptor of its own (scalar
+  // work); each lane's offset is recomputed from its lane id at load time (a few integer
+  // instructions) rather than held in registers across the loop.
+  __device__ __forceinline__ uint32_t k_off() const {
+    const int r8 = lane >> 3;
+    return (uint32_t)(r8 * (int)k_st_b) + 16u * ((lane & 7) ^ r8);
   }
-  __device__ __forceinline__ uint32_t v_lane_off(int i, int kb, bool clamp) const {
-    int r, c;
+  __device__ __forceinline__ uint32_t v_off(int hi) const {
     if (FP8V) {
-      r = 8 * (4 * wave + i) + (lane >> 3);
-      c = (lane & 7) ^ ((r & 3) | ((r >> 2) & 4));
-    } else {
-      r = 4 * (8 * wave + i) + (lane >> 4);
-      c = (lane & 15) ^ (2 * (r & 3));
+      const int r8 = lane >> 3;
+      return (uint32_t)(r8 * (int)v_st_b) + 16u * ((lane & 7) ^ ((r8 & 3) | (hi ? 4 : 0)));
     }
-    const int row = clamp ? min(r, Lk - 1 - kb) : r;
-    return (uint32_t)(row * (int)v_st_b) + 16u * c;
+    const int r4 = lane >> 4;
+    return (uint32_t)(r4 * (int)v_st_b) + 16u * ((lane & 15) ^ (2 * (r4 & 3)));
   }
 
-  __device__ __forceinline__ void dma_k(int blk, int buf) {
-    const int kb = blk * BN;
-    const bool clamp = kb + BN > Lk;
-    const uint8_t* base = kbase + (int64_t)kb * k_st_b;
+  // Buffer descriptor for [base, end): raw (stride 0), range = remaining bytes (clamped).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, const uint8_t* end) const {
+    const int64_t left = end - base;
+    const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
+  }
+
+  // K block b into K buffer buf of wave group tg (the issuing wave's group may differ; tg is a
+  // constant at every call).
+  __device__ __forceinline__ void dma_k(int tg, int b, int buf) {
+    uint8_t* area = lds + (tg - grp) * L::GROUP_BYTES;
+    const uint8_t* row0 = kbase + (int64_t)(b * BN + 32 * wave) * k_st_b;
+    LDS uint8_t* dst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 4 * wave * 1024);
+    const uint32_t off = k_off();
+    const auto r = rsrc(row0, p.k_end);  // one descriptor per block; the row step goes into the offsets
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int R = 4 * wave + i;               // 1 KB region = 8 key rows
-      __builtin_amdgcn_global_load_lds(base + k_lane_off(i, kb, clamp),
-                                       LDS_PTR(void, lds + L::OFF_K + buf * L::K_BYTES + R * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                               off + (uint32_t)(8 * i) * (uint32_t)k_st_b, 0, 0, 0);
     if (MX && wave < 2) {
-      const int row = min(kb + 64 * wave + lane, Lk - 1);
-      __builtin_amdgcn_global_load_lds(ksc_base + (uint32_t)(row * H * 4),
-                                       LDS_PTR(void, lds + L::OFF_KSC + buf * L::KSC_BYTES + wave * 256), 4, 0, 0);
+      const auto rs = rsrc(ksc_base + (int64_t)(b * BN + 64 * wave) * H * 4, ksc_base + (int64_t)(b * BN + BN) * H * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(area + L::OFF_KSC + buf * L::KSC_BYTES + wave * 256), 4,
+                                               (uint32_t)(lane * H * 4), 0, 0, 0);
     }
   }
 
-  __device__ __forceinline__ void dma_v(int blk, int buf) {
-    const int kb = blk * BN;
-    const bool clamp = kb + BN > Lk;
-    const uint8_t* base = vbase + (int64_t)kb * v_st_b;
-    constexpr int N = FP8V ? 4 : 8;             // 1 KB regions per wave
+  // V block b into V buffer y of static object obj (a constant at every call).
+  __device__ __forceinline__ void dma_v(int obj, int b, int y) {
+    constexpr int N = FP8V ? 4 : 8;              // 1 KB regions per wave
+    constexpr int ROWS = FP8V ? 8 : 4;           // key rows per region
+    LDS uint8_t* dst = (obj == 0 ? vobj[0] : vobj[1]) + y * L::V_BYTES + N * wave * 1024;
+    const uint8_t* row0 = vbase + (int64_t)(b * BN + N * ROWS * wave) * v_st_b;
+    const uint32_t off0 = v_off(0), off1 = FP8V ? v_off(1) : off0;
+    const auto r = rsrc(row0, p.v_end);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int R = N * wave + i;
-      __builtin_amdgcn_global_load_lds(base + v_lane_off(i, kb, clamp),
-                                       LDS_PTR(void, lds + L::OFF_V + buf * L::V_BYTES + R * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                               ((FP8V && (i & 2)) ? off1 : off0) + (uint32_t)(ROWS * i) * (uint32_t)v_st_b,
+                                               0, 0, 0);
   }
 
   // ---------------------------------------------------------------- precision guard
@@ -242,30 +308,45 @@ struct Attn {
     float kbound = 448.0f;
     if (MX) {
       uint32_t m = 0;
-      for (int row = threadIdx.x; row < Lk; row += 256) {
+      for (int row = threadIdx.x; row < Lk; row += 256 * G) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4);
         m = max(m, max(max(w & 0xFF, (w >> 8) & 0xFF), max((w >> 16) & 0xFF, w >> 24)));
       }
       kbound = 448.0f * e8m0_to_float(wave_max_u32(m));
     }
-    float b = c * qbound * kbound;       // per wave
-    if (lane == 0) red[wave] = b;
+    // per-wave bounds (each wave scanned a share of the key rows) -> workgroup maxima
+    if (lane == 0) {
+      red[threadIdx.x >> 6] = qbound;
+      red[8 + (threadIdx.x >> 6)] = kbound;
+    }
     __syncthreads();
-    b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float qb = 0.0f, kb = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4 * G; ++w) {
+      qb = fmaxf(qb, red[w]);
+      kb = fmaxf(kb, red[8 + w]);
+    }
     __syncthreads();
-    return b <= GUARD_LOG2;
+    return c * qb * kb <= GUARD_LOG2;
   }
 
   // ---------------------------------------------------------------- scores
+  // This wave's Q fragment for query tile nt (16 queries), from LDS.
+  __device__ __forceinline__ v8i q_frag(int nt) const {
+    LDS const v4u_t* qa = lds_at<const v4u_t>(lds_base - grp * L::GROUP_BYTES + L::OFF_Q + (wave * 2 + nt) * 2048 + lane * 16);
+    return make_v8i(qa[0], qa[64]);   // + 1024 bytes
+  }
+
   __device__ __forceinline__ void scores_fp8(int buf, v4f s[8][2]) {
+    const v8i qf[2] = {q_frag(0), q_frag(1)};
     const uint32_t kt = lds_base + L::OFF_K + buf * L::K_BYTES;
-    LDS const uint32_t* ksc = lds_at<const uint32_t>(lds_base + L::OFF_KSC + buf * L::KSC_BYTES);
+    LDS const uint8_t* ksc = lds_at<const uint8_t>(lds_base + L::OFF_KSC + buf * L::KSC_BYTES + 4 * n16 + g);
     LDS const v4u_t* k_a = lds_at<const v4u_t>(kt + n16 * 128 + ((g ^ (n16 & 7)) << 4));
     LDS const v4u_t* k_b = lds_at<const v4u_t>(kt + n16 * 128 + (((4 + g) ^ (n16 & 7)) << 4));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const v8i kf = make_v8i(k_a[mt * 128], k_b[mt * 128]);
-      const int ks = MX ? (int)((ksc[16 * mt + n16] >> (8 * g)) & 0xFFu) : 127;
+      const int ks = MX ? (int)ksc[64 * mt] : 127;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         s[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[nt], v4f{0.0f, 0.0f, 0.0f, 0.0f},
@@ -273,46 +354,52 @@ struct Attn {
     }
   }
 
+  // Guarded path: scores from exactly dequantized BF16 operands, one 32-wide slice of head_dim
+  // at a time (Q's slice reloaded from global memory, so only 8 registers hold it).
   __device__ __forceinline__ void scores_bf16(int buf, v4f s[8][2]) {
     const uint8_t* kt = lds + L::OFF_K + buf * L::K_BYTES;
     const uint32_t* ksc = reinterpret_cast<const uint32_t*>(lds + L::OFF_KSC + buf * L::KSC_BYTES);
-    v8bf qb[2][4];  // B operand: lane (n, g) holds d = 32u + 8g + 0..7, exactly dequantized
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int u = 0; u < 4; ++u) {
+      v8bf qb[2];  // B operand: lane (n, g) holds d = 32u + 8g + 0..7
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int nt = 0; nt < 2; ++nt) {
         uint2 w = make_uint2(0, 0);
         if (qrow[nt] != nullptr) w = ldg8(qrow[nt] + 32 * u + 8 * g);
-        qb[nt][u] = fp8x8_to_bf16(w.x, w.y, e8m0_to_float((qsw[nt] >> (8 * u)) & 0xFFu));
+        qb[nt] = fp8x8_to_bf16(w.x, w.y, e8m0_to_float((qsw[nt] >> (8 * u)) & 0xFFu));
       }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int r = 16 * mt + n16;
-      const uint32_t sw = MX ? ksc[r] : 0x7F7F7F7Fu;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int mt = 0; mt < 8; ++mt) {
+        const int r = 16 * mt + n16;
+        const uint32_t sw = MX ? ksc[r] : 0x7F7F7F7Fu;
         const int chunk = (2 * u + (g >> 1)) ^ (n16 & 7);
         const uint2 w = *reinterpret_cast<const uint2*>(kt + r * 128 + chunk * 16 + 8 * (g & 1));
         const v8bf kf = fp8x8_to_bf16(w.x, w.y, e8m0_to_float((sw >> (8 * u)) & 0xFFu));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb[nt][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[mt][nt], 0, 0, 0);
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb[nt], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[mt][nt], 0, 0, 0);
       }
     }
   }
 
   // ---------------------------------------------------------------- P V
-  // P fragments: fp8 mode one v8i per query tile (byte 4*mt + i = key 16*mt + 4*g + i);
-  // bf16 mode 4 chunks of 32 keys, 4 words each (element j = key 32u + 16*(j/4) + 4*g + j%4).
-  struct PFrag {
-    v8i f8[2];
-    uint32_t b16w[4][2][4];
-  };
+  // O^T d tile dt += V^T P^T for the block in the V buffer at v_lane (this lane's LDS byte
+  // address for d tile 0), V read transposed from the natural-layout tile.
+  // fp8 V^T fragment of d tile dt (4 transposed reads)
+  __device__ __forceinline__ v8i v_frag8(uint32_t v_lane, int dt, int jj) const {
+    LDS v2i_t* base = lds_at<v2i_t>(v_lane + ((dt ^ jj) << 4));
+    v8i vf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v2i_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(base + r * 512);  // + r * 4096 bytes
+      vf[2 * r] = w[0];
+      vf[2 * r + 1] = w[1];
+    }
+    return vf;
+  }
 
-  // O^T d tile dt += V(j-1)^T P(j-1)^T, V read transposed from the natural-layout LDS tile.
-  // v_lane: this lane's LDS byte address inside the V buffer for d tile 0 (see pv()).
-  __device__ __forceinline__ void pv_tile(uint32_t v_lane, int dt, int jj, const PFrag& pf) {
-    if (FP8V) {
+  __device__ __forceinline__ void pv_tile(uint32_t v_lane, int dt, int jj, const PF& pf) {
+    if constexpr (FP8V) {
       LDS v2i_t* base = lds_at<v2i_t>(v_lane + ((dt ^ jj) << 4));
       v8i vf;
 #pragma unroll
@@ -333,15 +420,16 @@ struct Attn {
         const v8bf vf = __builtin_bit_cast(v8bf, make_uint4(w0[0], w0[1], w1[0], w1[1]));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const uint4 w = make_uint4(pf.b16w[u][nt][0], pf.b16w[u][nt][1], pf.b16w[u][nt][2], pf.b16w[u][nt][3]);
+          const uint4 w = make_uint4(pf.w[u][nt][0], pf.w[u][nt][1], pf.w[u][nt][2], pf.w[u][nt][3]);
           o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(v8bf, w), o[dt][nt], 0, 0, 0);
         }
       }
     }
   }
 
-  __device__ __forceinline__ uint32_t v_lane_addr(int buf) const {
-    const uint32_t vt = lds_base + L::OFF_V + buf * L::V_BYTES;
+  template <int OBJ>
+  __device__ __forceinline__ uint32_t v_lane_addr(int y) const {
+    const uint32_t vt = (uint32_t)(uintptr_t)vobj[OBJ] + y * L::V_BYTES;
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     return FP8V ? vt + (16 * (jj >> 2) + 4 * g + (jj & 3)) * 128 + 8 * (n16 & 1)
                 : vt + (4 * g + jj) * 256 + 8 * (n16 & 1) + 16 * ((n16 & 3) >> 1);
@@ -349,26 +437,51 @@ struct Attn {
 
   // o_sum += 1^T P^T: the rounded probabilities summed on the matrix core with an all-ones
   // V^T tile, so O can be normalised by exactly the weights it was accumulated with.
-  // Only the BF16 mode needs it: there the probabilities are taken against a stale maximum.
-  __device__ __forceinline__ void pv_sum(const PFrag& pf) {
-    if (!FP8V) {
+  __device__ __forceinline__ void pv_sum(const PF& pf) {
+    if constexpr (FP8V) {
+      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        o_sum[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf.f8[nt], o_sum[nt], 0, 0, 0, 127, 0, 127);
+    } else {
       const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const uint4 w = make_uint4(pf.b16w[u][nt][0], pf.b16w[u][nt][1], pf.b16w[u][nt][2], pf.b16w[u][nt][3]);
+          const uint4 w = make_uint4(pf.w[u][nt][0], pf.w[u][nt][1], pf.w[u][nt][2], pf.w[u][nt][3]);
           o_sum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(v8bf, w), o_sum[nt], 0, 0, 0);
         }
     }
   }
 
-  // P V of a whole block resident in V buffer `buf`.
-  __device__ __forceinline__ void pv(int buf, const PFrag& pf) {
-    const uint32_t v_lane = v_lane_addr(buf);
+  // P V of a whole block resident in V buffer `buf`. One scheduling region per d tile, so that
+  // the transposed V reads are not all hoisted ahead (that would hold 8 fragments at once).
+  template <int OBJ>
+  __device__ __forceinline__ void pv(int y, const PF& pf) {
+    const uint32_t v_lane = v_lane_addr<OBJ>(y);
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
+    if constexpr (FP8V) {
+      // software-pipelined: the transposed reads of d tile dt+1 are issued before the matrix
+      // instructions of tile dt, so their latency overlaps
+      v8i nxt = v_frag8(v_lane, 0, jj);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) pv_tile(v_lane, dt, jj, pf);
+      for (int dt = 0; dt < 8; ++dt) {
+        const v8i vf = nxt;
+        if (dt < 7) nxt = v_frag8(v_lane, dt + 1, jj);
+        region_end();
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          o[dt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, pf.f8[nt], o[dt][nt], 0, 0, 0, 127, 0, 127);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        pv_tile(v_lane, dt, jj, pf);
+        region_end();
+      }
+    }
     pv_sum(pf);
   }
 
@@ -381,15 +494,14 @@ struct Attn {
     for (int nt = 0; nt < 2; ++nt) o_sum[nt] *= alpha[nt];
   }
 
-  // ---------------------------------------------------------------- one pipeline iteration
-  // Softmax of block j (scores in s -> P(j) in pf_cur), scores of block j+1 written back into
-  // s (if DO_QK) and O += P(j-1) V(j-1) (if DO_PV). Issued as 8 slots: slot k turns score tile k
-  // into probabilities, then overwrites it with the next block's score tile k, and runs the
-  // P V instructions of d tile k, so matrix and vector work overlap and live ranges stay short.
-  template <bool DO_QK, bool DO_PV, bool MASK>
-  __device__ __forceinline__ void step(int j, v4f s[8][2], const PFrag& pf_prev, PFrag& pf_cur) {
+  // ---------------------------------------------------------------- two-group phases
+  // Softmax of key block b (scores in s): mask, lazy running maximum, O and the rounded sum
+  // rescaled at once when the maximum moves (O holds exactly the P V of the earlier blocks
+  // here), probabilities -> pf, unrounded row sums -> l_run.
+  template <bool MASK>
+  __device__ __forceinline__ void softmax(int b, v4f s[8][2], PF& pf) {
     if (MASK) {
-      const int kb = j * BN;
+      const int kb = b * BN;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -399,22 +511,115 @@ struct Attn {
             s[mt][1][i] = -INFINITY;
           }
     }
-    // Row maxima of block j. The running maximum m_run is only moved when some row of the wave
-    // exceeds it by more than Lazy<FP8V>::LOG2; otherwise probabilities are taken against the
-    // stale maximum (they stay <= 2^LOG2, well inside BF16 range) and O needs no rescale.
-    float rs[2] = {0.0f, 0.0f};
-    bool move = false;
     float cand[2];
+    bool move = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
+      float mx = fmaxf(s[0][nt][0], s[0][nt][1]);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
-        mx = fmaxf(fmaxf(mx, fmaxf(s[mt][nt][0], s[mt][nt][1])), fmaxf(s[mt][nt][2], s[mt][nt][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+        for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(s[mt][nt][i], s[mt][nt][i + 1]));
+      mx = xmax16_32(mx);
       cand[nt] = mx * c;
-      move = move || (cand[nt] > m_run[nt] + Lazy<FP8V>::LOG2);
+      move = move || (cand[nt] > m_run[nt] + LAZY_LOG2);
+    }
+    if (__ballot(move) != 0) {  // wave-uniform, rare after the first block
+      const bool first = m_run[0] == -INFINITY;
+      float alpha[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float m_new = fmaxf(m_run[nt], cand[nt]);
+        alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        l_run[nt] *= alpha[nt];
+        m_run[nt] = m_new;
+      }
+      if (!first) rescale(alpha);
+    }
+    const float m_use[2] = {m_run[0], m_run[1]};
+    float rs[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pk[i] = __builtin_amdgcn_exp2f(fmaf(s[k][nt][i], c, -m_use[nt]));
+          rs[nt] += pk[i];
+        }
+        if constexpr (FP8V) {
+          pf.f8[nt][k] = (int)cvt4_e4m3(pk[0], pk[1], pk[2], pk[3]);
+        } else {
+          pf.w[k >> 1][nt][2 * (k & 1)] = cvt_pk_bf16(pk[0], pk[1]);
+          pf.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(pk[2], pk[3]);
+        }
+      }
+    }
+    l_run[0] += rs[0];
+    l_run[1] += rs[1];
+  }
+
+  // FP8 scores of the block in K buffer kbuf into s, one key tile per scheduling region.
+  __device__ __forceinline__ void qk(int kbuf, v4f s[8][2]) {
+    const v8i qf[2] = {q_frag(0), q_frag(1)};
+    const uint32_t kt = lds_base + L::OFF_K + kbuf * L::K_BYTES;
+    LDS const uint8_t* ksc = lds_at<const uint8_t>(lds_base + L::OFF_KSC + kbuf * L::KSC_BYTES + 4 * n16 + g);
+    LDS const v4u_t* k_a = lds_at<const v4u_t>(kt + n16 * 128 + ((g ^ (n16 & 7)) << 4));
+    LDS const v4u_t* k_b = lds_at<const v4u_t>(kt + n16 * 128 + (((4 + g) ^ (n16 & 7)) << 4));
+    // software-pipelined like pv(): key tile t+1's reads go out before tile t's instructions
+    v8i kn = make_v8i(k_a[0], k_b[0]);
+    int ksn = MX ? (int)ksc[0] : 127;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const v8i kf = kn;
+      const int ks = ksn;
+      if (t < 7) {
+        kn = make_v8i(k_a[(t + 1) * 128], k_b[(t + 1) * 128]);      // + 2048 bytes per tile
+        ksn = MX ? (int)ksc[64 * (t + 1)] : 127;
+      }
+      region_end();
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        s[t][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[nt], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                    0, 0, 0, ks, 0, qsc[nt]);
+    }
+  }
+
+  // ---------------------------------------------------------------- one pipeline step
+  // Softmax of local block j (scores in s -> probabilities in pf_cur), scores of block j+1
+  // written back into s (if DO_QK) and O += P(j-1) V(j-1) (if DO_PV). Issued as 8 slots: slot k
+  // turns score tile k into probabilities, then overwrites it with the next block's score tile
+  // k, and runs the P V instructions of d tile k, so matrix and vector work overlap and live
+  // ranges stay short.
+  template <bool DO_QK, bool DO_PV, bool MASK, int PAR>
+  __device__ __forceinline__ void step(int j, v4f s[8][2], const PF& pf_prev, PF& pf_cur) {
+    if (MASK) {
+      const int kb = blk(j) * BN;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * mt + 4 * g + i >= Lk) {
+            s[mt][0][i] = -INFINITY;
+            s[mt][1][i] = -INFINITY;
+          }
+    }
+    // Row maxima of the block. The running maximum m_run only moves when some row of the wave
+    // exceeds it by more than LAZY_LOG2; otherwise the probabilities are taken against the stale
+    // maximum and O needs no rescale.
+    float cand[2];
+    bool move = false;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = fmaxf(s[0][nt][0], s[0][nt][1]);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(s[mt][nt][i], s[mt][nt][i + 1]));
+      mx = xmax16_32(mx);
+      cand[nt] = mx * c;
+      move = move || (cand[nt] > m_run[nt] + LAZY_LOG2);
     }
     // O still lacks P(j-1) V(j-1), which was taken against the old maximum: O is rescaled after
     // that product has been added (end of this step); l has no such lag.
@@ -433,12 +638,18 @@ struct Attn {
     const float m_use[2] = {m_run[0], m_run[1]};
 
     const uint32_t kt = lds_base + L::OFF_K + ((j + 1) & 1) * L::K_BYTES;
-    LDS const uint32_t* ksc = lds_at<const uint32_t>(lds_base + L::OFF_KSC + ((j + 1) & 1) * L::KSC_BYTES);
+    LDS const uint8_t* ksc = lds_at<const uint8_t>(lds_base + L::OFF_KSC + ((j + 1) & 1) * L::KSC_BYTES + 4 * n16 + g);
     LDS const v4u_t* k_a = lds_at<const v4u_t>(kt + n16 * 128 + ((g ^ (n16 & 7)) << 4));
     LDS const v4u_t* k_b = lds_at<const v4u_t>(kt + n16 * 128 + (((4 + g) ^ (n16 & 7)) << 4));
-    const uint32_t v_lane = v_lane_addr((j + 2) % 3);   // V(j-1)
+    const uint32_t v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
+    v8i qf[2];
+    if (DO_QK) {
+      qf[0] = q_frag(0);
+      qf[1] = q_frag(1);
+    }
 
+    float rs[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       // probabilities of score tile k of block j
@@ -450,20 +661,20 @@ struct Attn {
           s[k][nt][i] = pv;
           rs[nt] += pv;
         }
-      if (FP8V) {
+      if constexpr (FP8V) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           pf_cur.f8[nt][k] = (int)cvt4_e4m3(s[k][nt][0], s[k][nt][1], s[k][nt][2], s[k][nt][3]);
       } else {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          pf_cur.b16w[k >> 1][nt][2 * (k & 1)] = cvt_pk_bf16(s[k][nt][0], s[k][nt][1]);
-          pf_cur.b16w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(s[k][nt][2], s[k][nt][3]);
+          pf_cur.w[k >> 1][nt][2 * (k & 1)] = cvt_pk_bf16(s[k][nt][0], s[k][nt][1]);
+          pf_cur.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(s[k][nt][2], s[k][nt][3]);
         }
       }
       if (DO_QK) {  // scores of block j+1, key tile k (overwrites the consumed tile)
         const v8i kf = make_v8i(k_a[k * 128], k_b[k * 128]);            // + k * 2048 bytes
-        const int ks = MX ? (int)((ksc[16 * k + n16] >> (8 * g)) & 0xFFu) : 127;
+        const int ks = MX ? (int)ksc[64 * k] : 127;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           s[k][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[nt], v4f{0.0f, 0.0f, 0.0f, 0.0f},
@@ -480,34 +691,117 @@ struct Attn {
     if (moved && !first) rescale(alpha);
   }
 
-  // Iteration j: loads K(j+2) into K buffer j%2 and V(j+1) into V buffer (j+1)%3, the pipelined
-  // step (scores of block j+1 on the FP8 path when FAST, else by the BF16 path after the step),
-  // then waits for this iteration's loads and synchronises the workgroup.
-  template <bool FAST, bool FIRST, bool LAST>
-  __device__ __forceinline__ void iteration(int j, v4f s[8][2], PFrag& pf_prev, PFrag& pf_cur) {
-    if (j + 2 < nb) dma_k(j + 2, j & 1);
-    if (!LAST) dma_v(j + 1, (j + 1) % 3);
-    step<FAST && !LAST, !FIRST, LAST>(j, s, pf_prev, pf_cur);
+  // ---------------------------------------------------------------- key loop
+  // One group (BF16 V). Local iteration j = key block j: loads K of block j+2 into K buffer j%2
+  // (freed when the scores of block j were taken) and V of block j into V buffer j%2 (freed by
+  // the P V of block j-2 in the previous iteration), runs the pipelined step (scores of block j+1
+  // on the FP8 path when FAST, else by the BF16 path after the step; P V of block j-1 inside the
+  // step's slots), then waits for its loads and synchronises the workgroup.
+  // PAR = j % 2 (a constant: the V buffers are chosen at compile time).
+  template <bool FAST, bool FIRST, bool LAST, int PAR>
+  __device__ __forceinline__ void iteration1(int j, v4f s[8][2], const PF& pf_prev, PF& pf_cur) {
+    if (j + 2 < ng) dma_k(0, blk(j + 2), j & 1);
+    dma_v(PAR, blk(j), 0);
+    step<FAST && !LAST, !FIRST, LAST, PAR>(j, s, pf_prev, pf_cur);
     if (!FAST && !LAST) scores_bf16((j + 1) & 1, s);
-    pf_prev = pf_cur;
     wait_vm_all();
     __syncthreads();
   }
 
-  template <bool FAST>
-  __device__ __forceinline__ void main_loop() {
-    v4f s[8][2];
-    PFrag pf_prev, pf_cur;
-    if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
-    __syncthreads();  // K buffer 0 is reused for block 2
-    if (nb == 1) {
-      iteration<FAST, true, true>(0, s, pf_prev, pf_cur);
+  // Two groups (E4M3 V), local iteration j = key block blk(j) of this group. Both groups do
+  // one softmax (VALU phase) and the P V and score instructions (matrix phase) per iteration,
+  // in opposite order, so that on each SIMD one wave's softmax meets the other wave's matrix
+  // instructions:
+  //   group 0: softmax(j), P V(j), scores(j+1)
+  //   group 1: P V(j-1), scores(j), then the loads of both groups, then softmax(j)
+  // A wave's LDS reads must wait for every load into LDS that the wave itself has in flight, so
+  // group 1 issues all loads after its last LDS read of the iteration (they land during its
+  // softmax) and group 0 issues none. Targets: group 0's K(j+2) -> its K buffer j%2 and V(j+1)
+  // -> its V buffer (j+1)%2; group 1's K(j+1) -> (j+1)%2 and V(j) -> j%2: each was last read
+  // in the previous iteration. Every iteration ends with its loads complete and one barrier.
+  template <int GRP, bool FAST, bool FIRST, bool LAST>
+  __device__ __forceinline__ void iteration2(int j, v4f s[8][2], PF& pf) {
+    if constexpr (GRP == 0) {
+      softmax<LAST>(blk(j), s, pf);
+      pv<0>(j & 1, pf);
+      if (!LAST) {
+        if (FAST) qk((j + 1) & 1, s); else scores_bf16((j + 1) & 1, s);
+      }
     } else {
-      iteration<FAST, true, false>(0, s, pf_prev, pf_cur);
-      for (int j = 1; j < nb - 1; ++j) iteration<FAST, false, false>(j, s, pf_prev, pf_cur);
-      iteration<FAST, false, true>(nb - 1, s, pf_prev, pf_cur);
+      if (!FIRST) pv<1>((j + 1) & 1, pf);
+      if (FAST) qk(j & 1, s); else scores_bf16(j & 1, s);
+      const int ng0 = ng + (nb & 1);  // group 0 has the extra block when nb is odd
+      if (j + 2 < ng0) dma_k(0, 2 * (j + 2), j & 1);
+      if (j + 1 < ng0) dma_v(0, 2 * (j + 1), (j + 1) & 1);
+      if (j + 1 < ng) dma_k(1, 2 * (j + 1) + 1, (j + 1) & 1);
+      dma_v(1, 2 * j + 1, j & 1);
+      softmax<LAST>(blk(j), s, pf);
     }
-    pv((nb - 1) % 3, pf_prev);   // the last block's P V (pf_prev holds P(nb-1) now)
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  // niter: iterations of the group with the most blocks; a group with fewer blocks only takes
+  // part in the barriers of the remaining iterations.
+  template <bool FAST>
+  __device__ __forceinline__ void main_loop(int niter) {
+    v4f s[8][2];
+    if (ng > 0 && grp == 0) {  // group 1 takes its first scores inside its first iteration
+      if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
+    }
+    __syncthreads();  // K buffer 0 is reused for blk(2)
+    int j = 0;
+    if constexpr (G == 1) {
+      // iteration j writes its probabilities to pa (j even) or pb (j odd) and reads the
+      // previous block's from the other set
+      PF pa, pb;
+      if (ng == 1) {
+        iteration1<FAST, true, true, 0>(0, s, pb, pa);
+      } else {
+        iteration1<FAST, true, false, 0>(0, s, pb, pa);
+        for (j = 1; j + 1 < ng - 1; j += 2) {
+          iteration1<FAST, false, false, 1>(j, s, pa, pb);
+          iteration1<FAST, false, false, 0>(j + 1, s, pb, pa);
+        }
+        if (j == ng - 2) {
+          iteration1<FAST, false, false, 1>(j, s, pa, pb);
+          iteration1<FAST, false, true, 0>(j + 1, s, pb, pa);
+        } else {
+          iteration1<FAST, false, true, 1>(j, s, pa, pb);
+        }
+      }
+      // the last block's P V (V buffer (ng-1)%2; probabilities in pa when ng is odd, else pb)
+      if (ng & 1) pv<0>(0, pa);
+      else pv<1>(0, pb);
+    } else {
+      // separate loops per group (the order of work differs), each register-allocated alone
+      if (grp == 0) loop2<0, FAST>(s, niter); else loop2<1, FAST>(s, niter);
+    }
+  }
+
+  template <int GRP, bool FAST>
+  __device__ __forceinline__ void loop2(v4f s[8][2], int niter) {
+    PF pf;
+    int j = 0;
+    if (ng == 1) {
+      iteration2<GRP, FAST, true, true>(0, s, pf);
+      j = 1;
+    } else if (ng > 1) {
+      iteration2<GRP, FAST, true, false>(0, s, pf);
+      for (j = 1; j < ng - 1; ++j) iteration2<GRP, FAST, false, false>(j, s, pf);
+      iteration2<GRP, FAST, false, true>(ng - 1, s, pf);
+      j = ng;
+    }
+    // group 1 still owes the P V of its last block: in the spare iteration if there is one
+    bool owed = GRP == 1 && ng > 0;
+    for (; j < niter; ++j) {
+      if (owed) {
+        pv<GRP>((ng - 1) & 1, pf);
+        owed = false;
+      }
+      __syncthreads();
+    }
+    if (owed) pv<GRP>((ng - 1) & 1, pf);
   }
 
   __device__ __forceinline__ void run(int qtile) {
@@ -518,9 +812,13 @@ struct Attn {
     const int k_start = p.cu_k[seq];
     Lk = p.cu_k[seq + 1] - k_start;
     nb = (Lk + BN - 1) / BN;
-    const int tid = threadIdx.x;
+    ng = (nb - grp + G - 1) / G;
+    const int niter = (nb + G - 1) / G;
+    const int tid = threadIdx.x & 255;
     lane = tid & 63;
-    wave = tid >> 6;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it (and everything
+    // derived from it: buffer offsets, branches, loop bounds) in scalar registers
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     n16 = lane & 15;
     g = lane >> 4;
 
@@ -535,14 +833,19 @@ struct Attn {
     ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
 
     // start the first loads before touching Q
-    if (nb > 0) {
-      dma_k(0, 0);
-      dma_v(0, 0);
-      if (nb > 1) dma_k(1, 1);
+    if (ng > 0) {
+      if (grp == 0) {
+        dma_k(0, blk(0), 0);
+        if (ng > 1) dma_k(0, blk(1), 1);
+        if (G == 2) dma_v(0, blk(0), 0);
+      } else {
+        dma_k(1, blk(0), 0);
+      }
     }
 
-    // ---- Q fragments: FP8 (score B operand) and exactly dequantized BF16 (guarded path) ----
+    // ---- Q fragments: FP8 (score B operand); the guarded path reloads them as BF16 ----
     uint32_t qmax_code = 0, qmax_scale = 0;
+    v8i qf[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int qi = q0 + wave * 32 + nt * 16 + n16;
@@ -569,6 +872,14 @@ struct Attn {
         qsw[nt] = 0x7F7F7F7Fu;
       }
     }
+    if (grp == 0) {  // both groups hold the same queries: group 0 stores the fragments
+      LDS v4u_t* qa = lds_at<v4u_t>(lds_base + L::OFF_Q + wave * 2 * 2048 + lane * 16);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        qa[nt * 128] = v4u_t{(unsigned)qf[nt][0], (unsigned)qf[nt][1], (unsigned)qf[nt][2], (unsigned)qf[nt][3]};
+        qa[nt * 128 + 64] = v4u_t{(unsigned)qf[nt][4], (unsigned)qf[nt][5], (unsigned)qf[nt][6], (unsigned)qf[nt][7]};
+      }
+    }
     if (MX) {
       qbound = 448.0f * e8m0_to_float(wave_max_u32(qmax_scale));
     } else {
@@ -586,13 +897,51 @@ struct Attn {
     o_sum[0] = o_sum[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (nb > 0) {
-      const bool fast = fp8_scores_ok_tile(reinterpret_cast<float*>(lds + L::TOTAL - 16));
+      const bool fast = fp8_scores_ok_tile(reinterpret_cast<float*>(lds - grp * L::GROUP_BYTES + L::OFF_RED));
       wait_vm_all();
       __syncthreads();
-      if (fast) main_loop<true>(); else main_loop<false>();
+      if (fast) main_loop<true>(niter); else main_loop<false>(niter);
     }
 
-    // ---- epilogue: O = O^T / l * vd -> BF16; LSE = ln2 * (m + log2 l) ----
+    if (G == 2) {
+      if (nb > 0) {
+        // Merge the two groups' partial results: group 1 leaves (m, l, O, rounded sum) in LDS,
+        // group 0 takes m = max(m0, m1) and adds each part scaled by 2^(m_g - m).
+        LDS v4f* area = reinterpret_cast<LDS v4f*>((wave < 2 ? vobj[0] : vobj[1]) + (wave & 1) * (L::VOBJ_BYTES / 2)) + lane;
+        LDS v4f* extra = reinterpret_cast<LDS v4f*>(LDS_PTR(uint8_t, lds - grp * L::GROUP_BYTES)) + wave * 2 * 64 + lane;
+        __syncthreads();  // every buffer read of the main loop is done
+        if (grp == 1) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) area[(2 * dt + nt) * 64] = o[dt][nt];
+          extra[0] = v4f{m_run[0], m_run[1], l_run[0], l_run[1]};
+          extra[64] = v4f{o_sum[0][0], o_sum[1][0], 0.0f, 0.0f};
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const v4f ml = extra[0];
+        const v4f os = extra[64];
+        float a0[2], a1[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float m = fmaxf(m_run[nt], ml[nt]);     // finite: group 0 has at least one block
+          a0[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m);
+          a1[nt] = __builtin_amdgcn_exp2f(ml[nt] - m);  // 0 when group 1 had no block (-inf)
+          l_run[nt] = l_run[nt] * a0[nt] + ml[2 + nt] * a1[nt];
+          o_sum[nt][0] = o_sum[nt][0] * a0[nt] + os[nt] * a1[nt];
+          m_run[nt] = m;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) o[dt][nt] = o[dt][nt] * a0[nt] + area[(2 * dt + nt) * 64] * a1[nt];
+      } else if (grp == 1) {
+        return;
+      }
+    }
+
+    // ---- epilogue: O = O^T / (rounded sum) * vd -> BF16; LSE = ln2 * (m + log2 l) ----
     const float vd = p.v_descale ? p.v_descale[seq * p.vd_ss + head * p.vd_sh] : 1.0f;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -600,9 +949,7 @@ struct Attn {
       lt += __shfl_xor(lt, 32);
       const int qi = q0 + wave * 32 + nt * 16 + n16;
       if (qi < Lq) {
-        // BF16 mode: the sum of the rounded probabilities (every row of the ones tile holds it);
-        // FP8 mode: the FP32 sum (the largest probability is exactly 1 there).
-        const float ls = FP8V ? lt : o_sum[nt][0];
+        const float ls = o_sum[nt][0];  // every row of the ones tile holds the rounded sum
         const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
         uint16_t* op = p.out + ((int64_t)(q_start + qi) * H + head) * 128 + 4 * g;
 #pragma unroll
@@ -621,7 +968,7 @@ struct Attn {
 };
 
 template <bool MX, bool FP8V>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   int seq, head, qtile;
   if (p.tile_order != nullptr) {
@@ -639,7 +986,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     seq = rest / p.num_heads;
   }
   if (qtile * BM >= p.cu_q[seq + 1] - p.cu_q[seq]) return;
-  Attn<MX, FP8V> a(p, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V>::VOBJ_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V>::VOBJ_BYTES];
+  Attn<MX, FP8V> a(p, smem, __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8)), LDS_PTR(uint8_t, va),
+                   LDS_PTR(uint8_t, vb));
   a.seq = seq;
   a.head = head;
   a.run(qtile);
@@ -650,6 +1000,7 @@ hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEven
   // Raising the dynamic LDS limit is a per-kernel, per-device attribute: done once per device.
   static std::atomic<uint64_t> configured{0};
   const int bytes = Lay<FP8V>::TOTAL;
+  const dim3 block(256 * Groups<FP8V>::G);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -661,13 +1012,13 @@ hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEven
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
   if (start == nullptr && stop == nullptr) {
-    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V>), grid, dim3(256), bytes, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V>), grid, block, bytes, s, p);
     return hipGetLastError();
   }
   // The dispatch itself stamps the events: their interval is the kernel, without launch gaps.
   AttnParams arg = p;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>), grid, dim3(256), args,
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>), grid, block, args,
                             bytes, s, start, stop, 0);
 }
 

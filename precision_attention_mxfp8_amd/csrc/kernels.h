@@ -46,6 +46,8 @@ struct AttnParams {
   const int32_t* tile_order;
   uint16_t* out;
   float* lse;
+  const uint8_t* k_end;  // one past the last byte of K / V: loads beyond read zeros
+  const uint8_t* v_end;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;  // elements
   int64_t qd_ss, qd_sh, kd_ss, kd_sh, vd_ss, vd_sh;
   int64_t total_q;
