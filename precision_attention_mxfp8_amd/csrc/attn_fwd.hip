@@ -308,9 +308,17 @@ struct Attn {
     float kbound = 448.0f;
     if (MX) {
       uint32_t m = 0;
-      for (int row = threadIdx.x; row < Lk; row += 256 * G) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4);
-        m = max(m, max(max(w & 0xFF, (w >> 8) & 0xFF), max((w >> 16) & 0xFF, w >> 24)));
+      // 8 independent loads in flight per thread and batch
+      for (int row0 = threadIdx.x; row0 < Lk; row0 += 8 * 256 * G) {
+        uint32_t w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = row0 + u * 256 * G;
+          w[u] = row < Lk ? *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          m = max(m, max(max(w[u] & 0xFF, (w[u] >> 8) & 0xFF), max((w[u] >> 16) & 0xFF, w[u] >> 24)));
       }
       kbound = 448.0f * e8m0_to_float(wave_max_u32(m));
     }
@@ -378,6 +386,7 @@ struct Attn {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb[nt], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[mt][nt], 0, 0, 0);
+        region_end();
       }
     }
   }
@@ -716,9 +725,10 @@ struct Attn {
   //   group 1: P V(j-1), scores(j), then the loads of both groups, then softmax(j)
   // A wave's LDS reads must wait for every load into LDS that the wave itself has in flight, so
   // group 1 issues all loads after its last LDS read of the iteration (they land during its
-  // softmax) and group 0 issues none. Targets: group 0's K(j+2) -> its K buffer j%2 and V(j+1)
-  // -> its V buffer (j+1)%2; group 1's K(j+1) -> (j+1)%2 and V(j) -> j%2: each was last read
-  // in the previous iteration. Every iteration ends with its loads complete and one barrier.
+  // softmax) and group 0 issues none (issuing group 0's own loads from group 0 instead slows its
+  // score phase). Targets: group 0's K(j+2) -> its K buffer j%2 and V(j+1) -> its V buffer
+  // (j+1)%2; group 1's K(j+1) -> (j+1)%2 and V(j) -> j%2: each was last read in the previous
+  // iteration. Every iteration ends with its loads complete and one barrier.
   template <int GRP, bool FAST, bool FIRST, bool LAST>
   __device__ __forceinline__ void iteration2(int j, v4f s[8][2], PF& pf) {
     if constexpr (GRP == 0) {
