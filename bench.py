@@ -7,10 +7,13 @@ benchmark quantizes once and builds metadata up front; here quantization is insi
 and is also reported on its own).
 
 Prints ONE JSON line: value = attention FLOPs (4 * Lq * Lk * H * D summed over sequences)
-per second of whole step; roofline = the attention kernel's own rate from HIP events that each of its
-dispatches in the timed region stamps at its start and end (hipExtLaunchKernel), against the
-dense FP8 matrix peak; cpu_baseline =
-the float64 CPU oracle on a bounded sample of the same workload.
+per second of whole step; roofline = the attention kernel's own rate from HIP events that its
+dispatch stamps at its start and end (hipExtLaunchKernel) in every --stamp-every'th step of the
+timed region, against the dense FP8 matrix peak (stamping a dispatch makes the runtime do about
+20 us of extra work for that step, so stamping all of them would slow the step being measured);
+quantizer_gbps / cast_e4m3_gbps = the quantizer and the V cast replayed from a HIP graph of many
+back-to-back launches (eager launches of these short kernels are bound by the host);
+cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
 """
@@ -59,6 +62,8 @@ def parse():
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (reference dispatch "
                          "for scaling HBM byte counters)")
+    ap.add_argument("--stamp-every", type=int, default=8,
+                    help="the attention dispatch of every n-th timed step stamps a HIP event pair")
     ap.add_argument("--b2b-iters", type=int, default=0,
                     help="launches in the back-to-back and quantizer-only loops (0: about half a second)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attn_traffic.json"),
@@ -137,8 +142,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps; HIP events bracket every attention launch ----
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # ---- timed region: exactly K steps; every n-th attention dispatch stamps an event pair ----
+    every = max(1, args.stamp_every)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range((args.steps + every - 1) // every)]
     for e0, e1 in evs:   # create the HIP events (torch creates them on first record)
         e0.record()
         e1.record()
@@ -148,7 +155,7 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        state["ev"] = evs[i]
+        state["ev"] = evs[i // every] if i % every == 0 else None
         step()
     stop.record()
     torch.cuda.synchronize()
@@ -159,7 +166,7 @@ def main():
     attn_avg_ms = float(np.mean(attn_ms))
     attn_med_ms = float(np.median(attn_ms))
     log(f"step {step_ms * 1e3:.2f} us (wall {wall / args.steps * 1e6:.2f} us), attention avg {attn_avg_ms * 1e3:.2f} us "
-        f"median {attn_med_ms * 1e3:.2f} us")
+        f"median {attn_med_ms * 1e3:.2f} us over {len(evs)} stamped dispatches")
 
     # ---- attention back-to-back (the pages' protocol: quantize once, time the forward) ----
     n_b2b = args.b2b_iters or max(10, min(2000, int(0.5 / max(attn_avg_ms * 1e-3, 1e-6))))
@@ -171,20 +178,17 @@ def main():
     torch.cuda.synchronize()
     b2b_ms = a.elapsed_time(b) / n_b2b
 
-    # ---- quantizer alone: Q and K back to back ----
-    quant_gbps = None
+    # ---- quantizer and V cast alone: graphs of back-to-back launches, replayed ----
+    quant_gbps = cast_gbps = None
     if not per_tensor:
-        n_q = args.b2b_iters or 200
-        a.record()
-        for _ in range(n_q):
-            lp.quantize_mxfp8_varlen(q, mq, out=qx)
-            lp.quantize_mxfp8_varlen(k, mk, out=kx)
-        b.record()
-        torch.cuda.synchronize()
-        qms = a.elapsed_time(b) / n_q
         qbytes = sum(t.numel() * 2 + t.numel() + m.total_scale_rows * wl.num_heads * 4
                      for t, m in ((q, mq), (k, mk)))
+        qms = graph_ms_per_call(torch, lambda: (lp.quantize_mxfp8_varlen(q, mq, out=qx),
+                                                lp.quantize_mxfp8_varlen(k, mk, out=kx)))
         quant_gbps = qbytes / (qms * 1e-3) / 1e9
+        if pv_mode == "fp8":
+            cms = graph_ms_per_call(torch, lambda: lp.cast_e4m3(v, out=vx))
+            cast_gbps = v.numel() * 3 / (cms * 1e-3) / 1e9
 
     # ---- pv bf16 variant of the same workload, for the record ----
     extra = {}
@@ -239,10 +243,30 @@ def main():
         "attention_kernel_us_avg": round(attn_avg_ms * 1e3, 3),
         "attention_kernel_us_median": round(attn_med_ms * 1e3, 3),
         "quantizer_gbps": None if quant_gbps is None else round(quant_gbps, 1),
+        "cast_e4m3_gbps": None if cast_gbps is None else round(cast_gbps, 1),
         "pct_fp8_peak": round(100 * achieved / FP8_PEAK_TFLOPS, 2),
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
+
+
+def graph_ms_per_call(torch, call, per_graph=25, replays=20):
+    """Milliseconds per `call` when `per_graph` calls captured in one HIP graph are replayed
+    `replays` times back to back (the calls record no memset and allocate nothing)."""
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(per_graph):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * per_graph)
 
 
 def kernel_source_hash() -> str:
