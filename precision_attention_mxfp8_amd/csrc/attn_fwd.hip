@@ -216,6 +216,7 @@ struct Attn {
   // ---- per-wave state ----
   int qsc[2];
   float qbound;              // max |q| bound of the wave's queries
+  uint32_t ksw[8];           // first batch of the guard's K scale words, loaded before Q
   const uint8_t* qrow[2];    // this lane's query rows (nullptr past the end)
   uint32_t qsw[2];           // their E8M0 scale words
   float m_run[2], l_run[2];
@@ -300,16 +301,30 @@ struct Attn {
   }
 
   // ---------------------------------------------------------------- precision guard
-  // True when the whole tile may use the FP8 score path: c * max|q| * max|k| <= GUARD_LOG2 with
+  // The whole tile may use the FP8 score path when c * max|q| * max|k| <= GUARD_LOG2 with
   // max|q| over the workgroup's queries and max|k| over all keys of the (sequence, head). In MX
   // mode both bounds come from the E8M0 scales (block maxima lie in (224, 448] * 2^e); in
   // per-tensor mode |q| is read from the codes and |k| is bounded by the E4M3 range.
-  __device__ __forceinline__ bool fp8_scores_ok_tile(float* red) {
+  // Three parts: the first batch of K scale words is loaded before any other load of the tile
+  // (its latency overlaps theirs); each wave publishes its bounds into the reduction slots before
+  // the barrier that precedes the key loop; every wave combines them after that barrier.
+  __device__ __forceinline__ void guard_prefetch() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (int)threadIdx.x + u * 256 * G;
+      ksw[u] = row < Lk ? *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4) : 0u;
+    }
+  }
+
+  __device__ __forceinline__ void guard_publish(float* red) {
     float kbound = 448.0f;
     if (MX) {
       uint32_t m = 0;
-      // 8 independent loads in flight per thread and batch
-      for (int row0 = threadIdx.x; row0 < Lk; row0 += 8 * 256 * G) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        m = max(m, max(max(ksw[u] & 0xFF, (ksw[u] >> 8) & 0xFF), max((ksw[u] >> 16) & 0xFF, ksw[u] >> 24)));
+      // further batches (keys beyond the first 8 * 256 * G), 8 independent loads in flight each
+      for (int row0 = threadIdx.x + 8 * 256 * G; row0 < Lk; row0 += 8 * 256 * G) {
         uint32_t w[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -322,19 +337,21 @@ struct Attn {
       }
       kbound = 448.0f * e8m0_to_float(wave_max_u32(m));
     }
-    // per-wave bounds (each wave scanned a share of the key rows) -> workgroup maxima
+    // per-wave bounds (each wave scanned a share of the key rows), combined after the
+    // workgroup's next barrier by fp8_scores_ok_tile
     if (lane == 0) {
       red[threadIdx.x >> 6] = qbound;
       red[8 + (threadIdx.x >> 6)] = kbound;
     }
-    __syncthreads();
+  }
+
+  __device__ __forceinline__ bool fp8_scores_ok_tile(const float* red) const {
     float qb = 0.0f, kb = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4 * G; ++w) {
       qb = fmaxf(qb, red[w]);
       kb = fmaxf(kb, red[8 + w]);
     }
-    __syncthreads();
     return c * qb * kb <= GUARD_LOG2;
   }
 
@@ -841,6 +858,7 @@ struct Attn {
     k_st_b = p.k_st;
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
+    if (MX) guard_prefetch();
 
     // start the first loads before touching Q
     if (ng > 0) {
@@ -907,9 +925,11 @@ struct Attn {
     o_sum[0] = o_sum[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (nb > 0) {
-      const bool fast = fp8_scores_ok_tile(reinterpret_cast<float*>(lds - grp * L::GROUP_BYTES + L::OFF_RED));
+      float* red = reinterpret_cast<float*>(lds - grp * L::GROUP_BYTES + L::OFF_RED);
+      guard_publish(red);
       wait_vm_all();
       __syncthreads();
+      const bool fast = fp8_scores_ok_tile(red);
       if (fast) main_loop<true>(niter); else main_loop<false>(niter);
     }
 
