@@ -233,6 +233,16 @@ struct Attn {
   // key block processed by this group in its local iteration i
   __device__ __forceinline__ int blk(int i) const { return G * i + grp; }
 
+  // One group: its LDS reads are addressed as a single opaque per-lane offset from their object
+  // (V object or dynamic area), so that the compiler can tell which object each read touches
+  // (it follows only a few address steps back to the object, and otherwise waits for every load
+  // into LDS in flight). The empty asm emits nothing; it only keeps the offset in one piece.
+  __device__ __forceinline__ static uint32_t opaque(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+  }
+  __device__ __forceinline__ LDS uint8_t* dyn() const { return LDS_PTR(uint8_t, lds); }
+
   // ---------------------------------------------------------------- global -> LDS
   // Buffer loads straight to LDS: the block's base (uniform) goes into a buffer descriptor
   // whose range ends at the tensor's last byte, so rows past the end of the last sequence
@@ -358,7 +368,11 @@ struct Attn {
   // ---------------------------------------------------------------- scores
   // This wave's Q fragment for query tile nt (16 queries), from LDS.
   __device__ __forceinline__ v8i q_frag(int nt) const {
-    LDS const v4u_t* qa = lds_at<const v4u_t>(lds_base - grp * L::GROUP_BYTES + L::OFF_Q + (wave * 2 + nt) * 2048 + lane * 16);
+    LDS const v4u_t* qa;
+    if constexpr (G == 1)
+      qa = reinterpret_cast<LDS const v4u_t*>(dyn() + opaque(L::OFF_Q + (wave * 2 + nt) * 2048 + lane * 16));
+    else
+      qa = lds_at<const v4u_t>(lds_base - grp * L::GROUP_BYTES + L::OFF_Q + (wave * 2 + nt) * 2048 + lane * 16);
     return make_v8i(qa[0], qa[64]);   // + 1024 bytes
   }
 
@@ -412,8 +426,8 @@ struct Attn {
   // O^T d tile dt += V^T P^T for the block in the V buffer at v_lane (this lane's LDS byte
   // address for d tile 0), V read transposed from the natural-layout tile.
   // fp8 V^T fragment of d tile dt (4 transposed reads)
-  __device__ __forceinline__ v8i v_frag8(uint32_t v_lane, int dt, int jj) const {
-    LDS v2i_t* base = lds_at<v2i_t>(v_lane + ((dt ^ jj) << 4));
+  __device__ __forceinline__ v8i v_frag8(LDS uint8_t* v_lane, int dt, int jj) const {
+    LDS v2i_t* base = reinterpret_cast<LDS v2i_t*>(v_lane + ((dt ^ jj) << 4));
     v8i vf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -424,9 +438,9 @@ struct Attn {
     return vf;
   }
 
-  __device__ __forceinline__ void pv_tile(uint32_t v_lane, int dt, int jj, const PF& pf) {
+  __device__ __forceinline__ void pv_tile(LDS uint8_t* v_lane, int dt, int jj, const PF& pf) {
     if constexpr (FP8V) {
-      LDS v2i_t* base = lds_at<v2i_t>(v_lane + ((dt ^ jj) << 4));
+      LDS v2i_t* base = reinterpret_cast<LDS v2i_t*>(v_lane + ((dt ^ jj) << 4));
       v8i vf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -438,7 +452,7 @@ struct Attn {
       for (int nt = 0; nt < 2; ++nt)
         o[dt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, pf.f8[nt], o[dt][nt], 0, 0, 0, 127, 0, 127);
     } else {
-      LDS v4s_t* base = lds_at<v4s_t>(v_lane + ((dt ^ jj) << 5));
+      LDS v4s_t* base = reinterpret_cast<LDS v4s_t*>(v_lane + ((dt ^ jj) << 5));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const v2u_t w0 = __builtin_bit_cast(v2u_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(base + (32 * u) * 32));  // (32u) rows * 256 B
@@ -453,12 +467,14 @@ struct Attn {
     }
   }
 
+  // this lane's LDS address for d tile 0 of V buffer y in V object OBJ
   template <int OBJ>
-  __device__ __forceinline__ uint32_t v_lane_addr(int y) const {
-    const uint32_t vt = (uint32_t)(uintptr_t)vobj[OBJ] + y * L::V_BYTES;
+  __device__ __forceinline__ LDS uint8_t* v_lane_addr(int y) const {
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
-    return FP8V ? vt + (16 * (jj >> 2) + 4 * g + (jj & 3)) * 128 + 8 * (n16 & 1)
-                : vt + (4 * g + jj) * 256 + 8 * (n16 & 1) + 16 * ((n16 & 3) >> 1);
+    const uint32_t off = y * L::V_BYTES + (FP8V ? (16 * (jj >> 2) + 4 * g + (jj & 3)) * 128 + 8 * (n16 & 1)
+                                                : (4 * g + jj) * 256 + 8 * (n16 & 1) + 16 * ((n16 & 3) >> 1));
+    if constexpr (G == 1) return vobj[OBJ] + opaque(off);
+    return lds_at<uint8_t>((uint32_t)(uintptr_t)vobj[OBJ] + off);
   }
 
   // o_sum += 1^T P^T: the rounded probabilities summed on the matrix core with an all-ones
@@ -486,7 +502,7 @@ struct Attn {
   // the transposed V reads are not all hoisted ahead (that would hold 8 fragments at once).
   template <int OBJ>
   __device__ __forceinline__ void pv(int y, const PF& pf) {
-    const uint32_t v_lane = v_lane_addr<OBJ>(y);
+    LDS uint8_t* v_lane = v_lane_addr<OBJ>(y);
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     if constexpr (FP8V) {
       // software-pipelined: the transposed reads of d tile dt+1 are issued before the matrix
@@ -663,11 +679,13 @@ struct Attn {
     }
     const float m_use[2] = {m_run[0], m_run[1]};
 
-    const uint32_t kt = lds_base + L::OFF_K + ((j + 1) & 1) * L::K_BYTES;
-    LDS const uint8_t* ksc = lds_at<const uint8_t>(lds_base + L::OFF_KSC + ((j + 1) & 1) * L::KSC_BYTES + 4 * n16 + g);
-    LDS const v4u_t* k_a = lds_at<const v4u_t>(kt + n16 * 128 + ((g ^ (n16 & 7)) << 4));
-    LDS const v4u_t* k_b = lds_at<const v4u_t>(kt + n16 * 128 + (((4 + g) ^ (n16 & 7)) << 4));
-    const uint32_t v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
+    const int kb1 = (j + 1) & 1;
+    LDS const uint8_t* ksc = dyn() + opaque(L::OFF_KSC + kb1 * L::KSC_BYTES + 4 * n16 + g);
+    LDS const v4u_t* k_a = reinterpret_cast<LDS const v4u_t*>(
+        dyn() + opaque(L::OFF_K + kb1 * L::K_BYTES + n16 * 128 + ((g ^ (n16 & 7)) << 4)));
+    LDS const v4u_t* k_b = reinterpret_cast<LDS const v4u_t*>(
+        dyn() + opaque(L::OFF_K + kb1 * L::K_BYTES + n16 * 128 + (((4 + g) ^ (n16 & 7)) << 4)));
+    LDS uint8_t* v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     v8i qf[2];
     if (DO_QK) {
