@@ -849,7 +849,14 @@ struct Attn {
     if (owed) pv<GRP>((ng - 1) & 1, pf);
   }
 
-  __device__ __forceinline__ void run(int qtile) {
+  // One query tile. The precision guard decides before the key loop between FP8 and BF16
+  // scores. MODE 2: both loops in this function. MODE 0: FP8 scores only; when the guard fails,
+  // every wave returns false with no load in flight and nothing written, and the caller runs the
+  // tile again with MODE 1 (BF16 scores, no guard), which always completes and returns true.
+  template <int MODE>
+  __device__ __forceinline__ bool run(int qtile) {
+    constexpr bool GUARD = MODE != 1;     // this call evaluates the guard
+    constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
     H = p.num_heads;
     const int q_start = p.cu_q[seq];
     const int Lq = p.cu_q[seq + 1] - q_start;
@@ -876,7 +883,7 @@ struct Attn {
     k_st_b = p.k_st;
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
-    if (MX) guard_prefetch();
+    if (MX && GUARD) guard_prefetch();
 
     // start the first loads before touching Q
     if (ng > 0) {
@@ -902,8 +909,10 @@ struct Attn {
         const uint32_t sw = MX ? *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)p.cu_scale_q[seq] + qi) * H + head) * 4)
                                : 0x7F7F7F7Fu;
         qsc[nt] = (int)((sw >> (8 * g)) & 0xFFu);
-        qrow[nt] = qp;
-        qsw[nt] = sw;
+        if (MAY_SLOW) {
+          qrow[nt] = qp;
+          qsw[nt] = sw;
+        }
         uint32_t words[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -914,8 +923,10 @@ struct Attn {
       } else {
         qf[nt] = make_v8i(make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0));
         qsc[nt] = 127;
-        qrow[nt] = nullptr;
-        qsw[nt] = 0x7F7F7F7Fu;
+        if (MAY_SLOW) {
+          qrow[nt] = nullptr;
+          qsw[nt] = 0x7F7F7F7Fu;
+        }
       }
     }
     if (grp == 0) {  // both groups hold the same queries: group 0 stores the fragments
@@ -926,7 +937,8 @@ struct Attn {
         qa[nt * 128 + 64] = v4u_t{(unsigned)qf[nt][4], (unsigned)qf[nt][5], (unsigned)qf[nt][6], (unsigned)qf[nt][7]};
       }
     }
-    if (MX) {
+    if (!GUARD) {
+    } else if (MX) {
       qbound = 448.0f * e8m0_to_float(wave_max_u32(qmax_scale));
     } else {
       // largest E4M3 magnitude among the wave's query codes (codes order like magnitudes)
@@ -944,11 +956,16 @@ struct Attn {
 
     if (nb > 0) {
       float* red = reinterpret_cast<float*>(lds - grp * L::GROUP_BYTES + L::OFF_RED);
-      guard_publish(red);
+      if (GUARD) guard_publish(red);
       wait_vm_all();
       __syncthreads();
-      const bool fast = fp8_scores_ok_tile(red);
-      if (fast) main_loop<true>(niter); else main_loop<false>(niter);
+      if (MODE == 1) {
+        main_loop<false>(niter);
+      } else {
+        const bool fast = fp8_scores_ok_tile(red);  // uniform: every wave reads the same slots
+        if (MODE == 0 && !fast) return false;
+        if (fast) main_loop<true>(niter); else main_loop<false>(niter);
+      }
     }
 
     if (G == 2) {
@@ -967,7 +984,7 @@ struct Attn {
           extra[64] = v4f{o_sum[0][0], o_sum[1][0], 0.0f, 0.0f};
         }
         __syncthreads();
-        if (grp == 1) return;
+        if (grp == 1) return true;
         const v4f ml = extra[0];
         const v4f os = extra[64];
         float a0[2], a1[2];
@@ -985,7 +1002,7 @@ struct Attn {
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) o[dt][nt] = o[dt][nt] * a0[nt] + area[(2 * dt + nt) * 64] * a1[nt];
       } else if (grp == 1) {
-        return;
+        return true;
       }
     }
 
@@ -1012,8 +1029,27 @@ struct Attn {
               lt > 0.0f ? (m_run[nt] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
       }
     }
+    return true;
   }
 };
+
+// A tile on the BF16 score path, in a function of its own so that the two-group kernel's FP8
+// path (256 registers per wave) is register-allocated without it: sharing one allocation costs
+// the FP8 path spills around its loops. Only tiles that fail the precision guard make the call
+// (which also saves the registers the calling convention asks the callee to preserve).
+template <bool MX, bool FP8V>
+__device__ __attribute__((noinline)) void slow_tile(const AttnParams* pp, uint8_t* smem, LDS uint8_t* va,
+                                                    LDS uint8_t* vb, int grp, int seq, int head, int qtile) {
+  // arguments arrive in vector registers: the uniform ones go back to scalar registers
+  const uint64_t pa = (uint64_t)(uintptr_t)pp;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+  const AttnParams& p = *reinterpret_cast<const AttnParams*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+  Attn<MX, FP8V> a(p, smem, __builtin_amdgcn_readfirstlane(grp), va, vb);
+  a.seq = __builtin_amdgcn_readfirstlane(seq);
+  a.head = __builtin_amdgcn_readfirstlane(head);
+  a.template run<1>(__builtin_amdgcn_readfirstlane(qtile));
+}
 
 template <bool MX, bool FP8V>
 __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnParams p) {
@@ -1036,11 +1072,23 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
   if (qtile * BM >= p.cu_q[seq + 1] - p.cu_q[seq]) return;
   __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V>::VOBJ_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V>::VOBJ_BYTES];
-  Attn<MX, FP8V> a(p, smem, __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8)), LDS_PTR(uint8_t, va),
-                   LDS_PTR(uint8_t, vb));
+  const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
+  Attn<MX, FP8V> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
   a.seq = seq;
   a.head = head;
-  a.run(qtile);
+  if constexpr (Groups<FP8V>::G == 1) {
+    a.template run<2>(qtile);  // 512 registers per wave: both score loops fit in one allocation
+  } else if (!a.template run<0>(qtile)) {
+    // The parameters are the kernel's only argument: the callee reads them in place in the
+    // kernel-argument segment (taking the address of p instead makes the kernel itself read its
+    // fields differently, to the FP8 loop's cost). The host compilation pass has no such segment.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const AttnParams* pp = reinterpret_cast<const AttnParams*>(__builtin_amdgcn_kernarg_segment_ptr());
+#else
+    const AttnParams* pp = nullptr;
+#endif
+    slow_tile<MX, FP8V>(pp, smem, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb), grp, seq, head, qtile);
+  }
 }
 
 template <bool MX, bool FP8V>
