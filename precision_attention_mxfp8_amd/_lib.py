@@ -55,6 +55,7 @@ class AttnArgs(ctypes.Structure):
         ("out", _p), ("lse", _p),
         ("tile_order", _p), ("num_tiles", _i32),
         ("start_event", _p), ("stop_event", _p),
+        ("k_scale_block_max", _p),
     ]
 
 
@@ -88,7 +89,7 @@ def load() -> ctypes.CDLL:
         lib.lpfa_last_error.argtypes = []
         lib.mxfp8_quantize_varlen.restype = ctypes.c_int
         lib.mxfp8_quantize_varlen.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
-                                              _i32, _i64, ctypes.c_int, _p, _p, _p]
+                                              _i32, _i64, ctypes.c_int, _p, _p, _p, _p]
         lib.lp_fp8_cast_e4m3.restype = ctypes.c_int
         lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p]
         lib.lp_attn_varlen_fwd.restype = ctypes.c_int

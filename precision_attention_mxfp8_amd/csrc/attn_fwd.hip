@@ -210,6 +210,7 @@ struct Attn {
   const uint8_t* vbase;      // value row 0 (bytes)
   int64_t k_st_b, v_st_b;    // row strides in bytes
   const uint8_t* ksc_base;   // scale word of key row 0 of this (sequence, head)
+  const uint8_t* kbm_base;   // K scale maximum of key block 0 of this (sequence, head), if given
   float c;                   // softmax_scale * log2(e) * qd * kd
 
 
@@ -318,11 +319,18 @@ struct Attn {
   // Three parts: the first batch of K scale words is loaded before any other load of the tile
   // (its latency overlaps theirs); each wave publishes its bounds into the reduction slots before
   // the barrier that precedes the key loop; every wave combines them after that barrier.
+  // The K data the guard reads: element i is the maximum scale byte of key block i (from the
+  // quantizer, when given: nb elements) or the scale word of key row i (Lk elements).
+  __device__ __forceinline__ int guard_count() const { return kbm_base ? nb : Lk; }
+  __device__ __forceinline__ uint32_t guard_elem(int i) const {
+    return kbm_base ? (uint32_t)kbm_base[(int64_t)i * H] : *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)i * H * 4);
+  }
   __device__ __forceinline__ void guard_prefetch() {
+    const int n = guard_count();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int row = (int)threadIdx.x + u * 256 * G;
-      ksw[u] = row < Lk ? *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4) : 0u;
+      const int i = (int)threadIdx.x + u * 256 * G;
+      ksw[u] = i < n ? guard_elem(i) : 0u;
     }
   }
 
@@ -333,13 +341,14 @@ struct Attn {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         m = max(m, max(max(ksw[u] & 0xFF, (ksw[u] >> 8) & 0xFF), max((ksw[u] >> 16) & 0xFF, ksw[u] >> 24)));
-      // further batches (keys beyond the first 8 * 256 * G), 8 independent loads in flight each
-      for (int row0 = threadIdx.x + 8 * 256 * G; row0 < Lk; row0 += 8 * 256 * G) {
+      // further batches (elements beyond the first 8 * 256 * G), 8 independent loads in flight each
+      const int n = guard_count();
+      for (int i0 = threadIdx.x + 8 * 256 * G; i0 < n; i0 += 8 * 256 * G) {
         uint32_t w[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int row = row0 + u * 256 * G;
-          w[u] = row < Lk ? *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)row * H * 4) : 0u;
+          const int i = i0 + u * 256 * G;
+          w[u] = i < n ? guard_elem(i) : 0u;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -883,6 +892,7 @@ struct Attn {
     k_st_b = p.k_st;
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
+    kbm_base = MX && p.k_bmax ? p.k_bmax + (int64_t)(p.cu_scale_k[seq] / BN) * H + head : nullptr;
     if (MX && GUARD) guard_prefetch();
 
     // start the first loads before touching Q

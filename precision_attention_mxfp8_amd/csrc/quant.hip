@@ -6,12 +6,15 @@
 // FastVideo fp8-PV PR (unscaled e4m3 cast of V).
 //
 // Work mapping (HBM-bound, one pass over the input):
-//   16 lanes own one (scale row, head) pair = 128 elements; each lane loads 8 consecutive
-//   elements with one 16-byte load (two for FP32). The 4 lanes of a 32-element block reduce
-//   their maximum with two cross-lane xor steps inside a quad (DPP), derive the exponent from
-//   the maximum's bits, scale by an exact power of two and convert with the hardware E4M3
-//   conversion (round to nearest even). Lane 0 of the 16 gathers the four scale bytes and
-//   writes them as one word. Pad rows of the scale storage get 0x7F and no payload.
+//   A workgroup owns one (128-row block of the scale storage, head) pair: 16 rows per pass, 8
+//   passes. 16 lanes own one (scale row, head) pair = 128 elements; each lane loads 8
+//   consecutive elements with one 16-byte load (two for FP32). The 4 lanes of a 32-element
+//   block reduce their maximum with two cross-lane xor steps inside a quad (DPP), derive the
+//   exponent from the maximum's bits, scale by an exact power of two and convert with the
+//   hardware E4M3 conversion (round to nearest even). Lane 0 of the 16 gathers the four scale
+//   bytes and writes them as one word. Pad rows of the scale storage get 0x7F and no payload.
+//   Optionally the workgroup also writes the largest scale byte of its block's real rows (one
+//   byte per block and head): the attention kernel's precision guard bounds |k| with it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -65,50 +68,68 @@ struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
 
 template <typename T>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t head_row = gid >> 4;  // (scale row, head) pair
-  const int sub = threadIdx.x & 15;   // 8-element chunk of the 128-element row
-  if (head_row >= p.total_scale_rows * p.num_heads) return;  // all 16 lanes of a row agree
-  const int64_t srow = head_row / p.num_heads;
-  const int h = (int)(head_row - srow * p.num_heads);
+  __shared__ uint32_t red[4];
+  const int h = (int)(blockIdx.x % (unsigned)p.num_heads);  // neighbouring workgroups: same rows
+  const int64_t blk = blockIdx.x / (unsigned)p.num_heads;
+  const int sub = threadIdx.x & 15;  // 8-element chunk of the 128-element row
+  const int64_t srow0 = blk * 128;
 
-  // sequence owning this scale row: the largest i with cu_scale[i] <= srow
+  // sequence owning this block (every block lies inside one sequence's padded rows): the
+  // largest i with cu_scale[i] <= srow0
   int lo = 0, hi = p.num_seqs;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if ((int64_t)p.cu_scale[mid] <= srow) lo = mid; else hi = mid;
+    if ((int64_t)p.cu_scale[mid] <= srow0) lo = mid; else hi = mid;
   }
-  const int64_t local = srow - p.cu_scale[lo];
+  const int64_t local0 = srow0 - p.cu_scale[lo];
   const int64_t seq_len = (int64_t)p.cu_seqlens[lo + 1] - p.cu_seqlens[lo];
-  uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
-  if (local >= seq_len) {  // pad row of the 128-token-padded scale storage
-    if (sub == 0) *scale_word = 0x7F7F7F7Fu;
-    return;
-  }
-  const int64_t t = p.cu_seqlens[lo] + local;
-
-  float v[8];
-  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // reduce over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the 16)
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  const int e = block_exponent(amax, p.scaling_mode);
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 120]: normal
-
-  uint32_t w0 = cvt4_e4m3(clamp448(v[0] * inv), clamp448(v[1] * inv), clamp448(v[2] * inv), clamp448(v[3] * inv));
-  uint32_t w1 = cvt4_e4m3(clamp448(v[4] * inv), clamp448(v[5] * inv), clamp448(v[6] * inv), clamp448(v[7] * inv));
-  *reinterpret_cast<uint2*>(p.payload + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
-
-  // gather the 4 block scale bytes of this row into lane 0 of the 16
-  const uint32_t sbyte = (uint32_t)(e + 127);
+  const int64_t t0 = p.cu_seqlens[lo] + local0;
   const int base = (threadIdx.x & 63) & ~15;
-  uint32_t b1 = __shfl(sbyte, base + 4);
-  uint32_t b2 = __shfl(sbyte, base + 8);
-  uint32_t b3 = __shfl(sbyte, base + 12);
-  if (sub == 0) *scale_word = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+
+  uint32_t smax = 0;
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int r = pass * 16 + (int)(threadIdx.x >> 4);  // row inside the block
+    const int64_t srow = srow0 + r;
+    uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
+    if (local0 + r >= seq_len) {  // pad row of the 128-token-padded scale storage
+      if (sub == 0) *scale_word = 0x7F7F7F7Fu;
+      continue;
+    }
+    const int64_t t = t0 + r;
+    float v[8];
+    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    // reduce over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the 16)
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int e = block_exponent(amax, p.scaling_mode);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 120]: normal
+
+    uint32_t w0 = cvt4_e4m3(clamp448(v[0] * inv), clamp448(v[1] * inv), clamp448(v[2] * inv), clamp448(v[3] * inv));
+    uint32_t w1 = cvt4_e4m3(clamp448(v[4] * inv), clamp448(v[5] * inv), clamp448(v[6] * inv), clamp448(v[7] * inv));
+    *reinterpret_cast<uint2*>(p.payload + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
+
+    // gather the 4 block scale bytes of this row into lane 0 of the 16 (all 16 lanes of a row
+    // take this branch together: the row decides it)
+    const uint32_t sbyte = (uint32_t)(e + 127);
+    smax = max(smax, sbyte);
+    uint32_t b1 = __shfl(sbyte, base + 4);
+    uint32_t b2 = __shfl(sbyte, base + 8);
+    uint32_t b3 = __shfl(sbyte, base + 12);
+    if (sub == 0) *scale_word = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+
+  if (p.block_max != nullptr) {  // uniform over the workgroup
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) smax = max(smax, (uint32_t)__shfl_xor((int)smax, s));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = smax;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      p.block_max[blk * p.num_heads + h] = (uint8_t)max(max(red[0], red[1]), max(red[2], red[3]));
+  }
 }
 
 template <typename T>
@@ -129,9 +150,9 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
 }  // namespace
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
-  const int64_t threads = p.total_scale_rows * p.num_heads * 16;
-  if (threads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t blocks = p.total_scale_rows / 128 * p.num_heads;  // scale rows: whole blocks
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
   if (p.x_dtype == LPFA_DTYPE_BF16)
     hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   else

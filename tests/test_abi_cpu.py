@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 1
+    assert lib.lpfa_abi_version() == 2
 
 
 def test_struct_layout_matches_c():
@@ -67,7 +67,7 @@ def _quant(lib, **kw):
                                      args["total_tokens"], args["num_heads"], args["head_dim"],
                                      args["cu_seqlens"], args["cu_scale"], args["num_seqs"],
                                      args["total_scale_rows"], args["scaling_mode"], args["payload"],
-                                     args["scales"], None)
+                                     args["scales"], None, None)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import precision_attention_mxfp8_amd as lp
-from synth import make_workload, make_custom, bf16_bits_to_f32
+from synth import make_workload, make_custom, bf16_bits_to_f32, f32_to_bf16_bits
 from helpers import bf16_to_device, f64
 
 pytestmark = pytest.mark.gpu
@@ -160,3 +160,59 @@ def test_deterministic_repeat():
     a = _gpu_quant(x, wl.lengths_q, "rceil")
     b = _gpu_quant(x, wl.lengths_q, "rceil")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _block_max_from_scales(scales: np.ndarray, lengths) -> np.ndarray:
+    """Largest scale byte of each (128-row scale block, head) over the block's real rows."""
+    rows, h, _ = scales.shape
+    valid = np.zeros(rows, dtype=bool)
+    start = 0
+    for n in lengths:
+        valid[start:start + n] = True
+        start += -(-n // 128) * 128
+    masked = np.where(valid[:, None, None], scales, 0).astype(np.uint8)
+    return masked.reshape(rows // 128, 128, h, 4).max(axis=(1, 3))
+
+
+@pytest.mark.parametrize("mode", ["rceil", "floor"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_block_max(mode, dtype):
+    """The quantizer's per-(128-row block, head) maximum scale byte equals the maximum of the
+    oracle's scale bytes over the block's real rows (pad rows, which hold 0x7F, excluded), with
+    ragged lengths, empty sequences and block exponents that differ from block to block."""
+    rng = np.random.default_rng(12)
+    lengths = [0, 300, 1, 128, 129, 0, 517]
+    h = 3
+    t = sum(lengths)
+    x = rng.standard_normal((t, h, 128)).astype(np.float32)
+    x *= np.exp2(rng.integers(-30, 30, size=(t, h, 4)).repeat(32, axis=2)).astype(np.float32)
+    x *= np.exp2(rng.integers(-40, 40, size=(t, 1, 1))).astype(np.float32)   # rows differ too
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        xd, xo = bf16_to_device(bits), f64(bits)
+    else:
+        xd, xo = torch.from_numpy(x).cuda(), x.astype(np.float64)
+    meta = lp.VarlenMeta.from_lengths(lengths, xd.device)
+    mx = lp.quantize_mxfp8_varlen(xd, meta, scaling_mode=mode)
+    torch.cuda.synchronize()
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    _, rs, _ = oracle.mx_quantize_varlen(xo, cu, mode)
+    assert np.array_equal(mx.scales.cpu().numpy(), rs)
+    got = mx.block_max.cpu().numpy()
+    want = _block_max_from_scales(rs, lengths)
+    assert got.shape == want.shape == (meta.total_scale_rows // 128, h)
+    assert np.array_equal(got, want)
+    # the maxima really differ across blocks and heads in this input
+    assert len(np.unique(want)) > 3
+
+
+def test_block_max_optional():
+    """Without a block_max buffer the quantizer writes payload and scales only, bit-identically."""
+    wl = make_custom([300, 77], [300, 77], heads=2, seed=13)
+    x = bf16_to_device(wl.q_bits)
+    meta = lp.VarlenMeta.from_lengths(wl.lengths_q, x.device)
+    a = lp.quantize_mxfp8_varlen(x, meta)
+    b = lp.quantize_mxfp8_varlen(x, meta, out=lp.Mxfp8Tensor(torch.empty_like(a.payload), torch.empty_like(a.scales), meta))
+    torch.cuda.synchronize()
+    assert b.block_max is None
+    assert torch.equal(a.payload, b.payload) and torch.equal(a.scales, b.scales)
