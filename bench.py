@@ -111,7 +111,7 @@ def main():
                             torch.empty((mq.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mq)
         kx = lp.Mxfp8Tensor(torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev),
                             torch.empty((mk.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mk,
-                            torch.empty((mk.total_scale_rows // 128, h), dtype=torch.uint8, device=dev))
+                            torch.empty((mk.total_scale_rows // 16, h), dtype=torch.uint8, device=dev))
     vx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev) if pv_mode == "fp8" else v
     plan = lp.AttnPlan(mq, mk, h, pv_mode=pv_mode, mx=not per_tensor, tile_order=order)
     out, lse = plan.out, plan.lse

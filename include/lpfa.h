@@ -87,11 +87,11 @@ const char* lpfa_last_error(void);
  *   total_scale_rows  cu_scale[num_seqs].
  *   payload      output uint8 (T, num_heads, 128), contiguous.
  *   scales       output uint8 (total_scale_rows, num_heads, 4), contiguous.
- *   block_max    optional output (NULL: not written) uint8 (total_scale_rows / 128, num_heads):
- *                entry [k, h] is the largest scale byte of head h over the rows of scale block
- *                k (rows 128k .. 128k+127) that are not pad rows. Every block holds at least
- *                one such row. Passed to lp_attn_varlen_fwd as k_scale_block_max for K, it
- *                replaces the attention kernel's scan of the K scales (same results).
+ *   group_max    optional output (NULL: not written) uint8 (total_scale_rows / 16, num_heads):
+ *                entry [k, h] is the largest scale byte of head h over the rows of 16-row group
+ *                k (rows 16k .. 16k+15) that are not pad rows, 0 if all of them are. Passed to
+ *                lp_attn_varlen_fwd as k_scale_group_max for K, it replaces the attention
+ *                kernel's scan of the K scales (same results).
  * Errors: LPFA_EINVAL for NULL pointers (unless the tensor is empty), negative sizes,
  * misalignment, bad enum values; LPFA_ENOTSUP for head_dim != 128.
  */
@@ -99,7 +99,7 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
                           int64_t total_tokens, int32_t num_heads, int32_t head_dim,
                           const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
                           int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
-                          uint8_t* scales, uint8_t* block_max, void* stream);
+                          uint8_t* scales, uint8_t* group_max, void* stream);
 
 /*
  * lp_fp8_cast_e4m3 - unscaled E4M3 cast (the fp8 PV mode's V).
@@ -188,12 +188,12 @@ typedef struct lpfa_attn_args {
   void* start_event;
   void* stop_event;
 
-  /* Optional (MX mode): the block_max output of mxfp8_quantize_varlen for K, uint8
-   * (cu_scale_k[num_seqs] / 128, num_heads). When set, the precision guard (which picks
+  /* Optional (MX mode): the group_max output of mxfp8_quantize_varlen for K, uint8
+   * (cu_scale_k[num_seqs] / 16, num_heads). When set, the precision guard (which picks
    * the FP8 or the BF16 score path of a query tile, from bounds on |q| and |k|) reads the
    * K bound there instead of scanning k_scale; the guard's decisions, and so the
    * results, are the same either way. Ignored in per-tensor mode. */
-  const uint8_t* k_scale_block_max;
+  const uint8_t* k_scale_group_max;
 } lpfa_attn_args;
 
 /*

@@ -55,7 +55,7 @@ class AttnArgs(ctypes.Structure):
         ("out", _p), ("lse", _p),
         ("tile_order", _p), ("num_tiles", _i32),
         ("start_event", _p), ("stop_event", _p),
-        ("k_scale_block_max", _p),
+        ("k_scale_group_max", _p),
     ]
 
 

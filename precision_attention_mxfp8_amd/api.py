@@ -89,14 +89,14 @@ class VarlenMeta:
 class Mxfp8Tensor:
     """MXFP8 operand: E4M3 payload (T, H, 128) uint8 and E8M0 scales (sum P(L_i), H, 4) uint8.
 
-    ``block_max`` (optional, (sum P(L_i) / 128, H) uint8): the largest scale byte of each 128-row
-    scale block over its real rows, written by the quantizer. Used for K by the attention's
-    precision guard (results are the same without it)."""
+    ``group_max`` (optional, (sum P(L_i) / 16, H) uint8): the largest scale byte of each 16-row
+    group of the scale storage over its real rows (0 for a group of pad rows only), written by the
+    quantizer. Used for K by the attention's precision guard (results are the same without it)."""
 
     payload: torch.Tensor
     scales: torch.Tensor
     meta: VarlenMeta
-    block_max: Optional[torch.Tensor] = None
+    group_max: Optional[torch.Tensor] = None
 
 
 def _check_rows(x: torch.Tensor, name: str) -> None:
@@ -135,23 +135,23 @@ def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str =
     t, h, _ = x.shape
     if t != meta.total_tokens:
         raise ValueError(f"x has {t} tokens, metadata says {meta.total_tokens}")
-    bshape = (meta.total_scale_rows // 128, h)
+    gshape = (meta.total_scale_rows // 16, h)
     if out is None:
         payload = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
         scales = torch.empty((meta.total_scale_rows, h, 4), dtype=torch.uint8, device=x.device)
-        block_max = torch.empty(bshape, dtype=torch.uint8, device=x.device)
-        out = Mxfp8Tensor(payload, scales, meta, block_max)
+        group_max = torch.empty(gshape, dtype=torch.uint8, device=x.device)
+        out = Mxfp8Tensor(payload, scales, meta, group_max)
     else:
         _check_out(out.payload, (t, h, HEAD_DIM), torch.uint8, x.device, "out.payload")
         _check_out(out.scales, (meta.total_scale_rows, h, 4), torch.uint8, x.device, "out.scales")
-        if out.block_max is not None:
-            _check_out(out.block_max, bshape, torch.uint8, x.device, "out.block_max")
+        if out.group_max is not None:
+            _check_out(out.group_max, gshape, torch.uint8, x.device, "out.group_max")
         if out.meta is not meta:
-            out = Mxfp8Tensor(out.payload, out.scales, meta, out.block_max)
+            out = Mxfp8Tensor(out.payload, out.scales, meta, out.group_max)
     rc = _lib.load().mxfp8_quantize_varlen(
         x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM, meta.cu_seqlens.data_ptr(),
         meta.cu_scale.data_ptr(), meta.num_seqs, meta.total_scale_rows, mode, out.payload.data_ptr(),
-        out.scales.data_ptr(), None if out.block_max is None else out.block_max.data_ptr(), _stream())
+        out.scales.data_ptr(), None if out.group_max is None else out.group_max.data_ptr(), _stream())
     if rc:
         _lib.check("mxfp8_quantize_varlen", rc)
     return out
@@ -308,13 +308,13 @@ class AttnPlan:
                 raise ValueError("q/k were quantized with different sequence metadata")
             qp, kp = q.payload, k.payload
             a.q_scale, a.k_scale = q.scales.data_ptr(), k.scales.data_ptr()
-            if k.block_max is not None:
-                bm, bshape = k.block_max, (self.meta_k.total_scale_rows // 128, self.num_heads)
-                if bm.shape != bshape or bm.dtype != torch.uint8 or not bm.is_contiguous() or bm.device != self._dev:
-                    raise ValueError(f"k.block_max must be a contiguous uint8 tensor of shape {bshape} on {self._dev}")
-                a.k_scale_block_max = bm.data_ptr()
+            if k.group_max is not None:
+                gm, gshape = k.group_max, (self.meta_k.total_scale_rows // 16, self.num_heads)
+                if gm.shape != gshape or gm.dtype != torch.uint8 or not gm.is_contiguous() or gm.device != self._dev:
+                    raise ValueError(f"k.group_max must be a contiguous uint8 tensor of shape {gshape} on {self._dev}")
+                a.k_scale_group_max = gm.data_ptr()
             else:
-                a.k_scale_block_max = None
+                a.k_scale_group_max = None
             if q.scales.shape != (self.meta_q.total_scale_rows, self.num_heads, 4) or \
                     k.scales.shape != (self.meta_k.total_scale_rows, self.num_heads, 4):
                 raise ValueError("scale tensors do not match the metadata")

@@ -28,7 +28,7 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
                           int64_t total_tokens, int32_t num_heads, int32_t head_dim,
                           const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
                           int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
-                          uint8_t* scales, uint8_t* block_max, void* stream) {
+                          uint8_t* scales, uint8_t* group_max, void* stream) {
   if (int rc = lpfa::check_quantize(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads,
                                     head_dim, cu_seqlens, cu_scale, num_seqs, total_scale_rows,
                                     scaling_mode, payload, scales))
@@ -46,7 +46,7 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
   p.cu_scale = cu_scale;
   p.payload = payload;
   p.scales = scales;
-  p.block_max = block_max;
+  p.group_max = group_max;
   return launch_status(lpfa::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize");
 }
 
@@ -102,7 +102,7 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
     const int64_t kspan = a->total_k > 0 ? (a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128 : 0;
     const int64_t vspan = a->total_k > 0 ? ((a->total_k - 1) * a->v_stride_tok + (int64_t)(a->num_heads - 1) * a->v_stride_head + 128) * vb : 0;
     p.k_end = a->k + kspan;
-    p.k_bmax = a->q_scale != nullptr ? a->k_scale_block_max : nullptr;
+    p.k_gmax = a->q_scale != nullptr ? a->k_scale_group_max : nullptr;
     p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
   }
   p.total_q = a->total_q;

@@ -210,7 +210,7 @@ struct Attn {
   const uint8_t* vbase;      // value row 0 (bytes)
   int64_t k_st_b, v_st_b;    // row strides in bytes
   const uint8_t* ksc_base;   // scale word of key row 0 of this (sequence, head)
-  const uint8_t* kbm_base;   // K scale maximum of key block 0 of this (sequence, head), if given
+  const uint8_t* kgm_base;   // K scale maximum of key rows 0..15 of this (sequence, head), if given
   float c;                   // softmax_scale * log2(e) * qd * kd
 
 
@@ -319,11 +319,11 @@ struct Attn {
   // Three parts: the first batch of K scale words is loaded before any other load of the tile
   // (its latency overlaps theirs); each wave publishes its bounds into the reduction slots before
   // the barrier that precedes the key loop; every wave combines them after that barrier.
-  // The K data the guard reads: element i is the maximum scale byte of key block i (from the
-  // quantizer, when given: nb elements) or the scale word of key row i (Lk elements).
-  __device__ __forceinline__ int guard_count() const { return kbm_base ? nb : Lk; }
+  // The K data the guard reads: element i is the maximum scale byte of key rows 16i..16i+15
+  // (from the quantizer, when given: ceil(Lk/16) elements) or the scale word of key row i (Lk).
+  __device__ __forceinline__ int guard_count() const { return kgm_base ? (Lk + 15) / 16 : Lk; }
   __device__ __forceinline__ uint32_t guard_elem(int i) const {
-    return kbm_base ? (uint32_t)kbm_base[(int64_t)i * H] : *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)i * H * 4);
+    return kgm_base ? (uint32_t)kgm_base[(int64_t)i * H] : *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)i * H * 4);
   }
   __device__ __forceinline__ void guard_prefetch() {
     const int n = guard_count();
@@ -892,7 +892,7 @@ struct Attn {
     k_st_b = p.k_st;
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
-    kbm_base = MX && p.k_bmax ? p.k_bmax + (int64_t)(p.cu_scale_k[seq] / BN) * H + head : nullptr;
+    kgm_base = MX && p.k_gmax ? p.k_gmax + (int64_t)(p.cu_scale_k[seq] / 16) * H + head : nullptr;
     if (MX && GUARD) guard_prefetch();
 
     // start the first loads before touching Q

@@ -19,7 +19,7 @@ struct QuantParams {
   const int32_t* cu_scale;
   uint8_t* payload;
   uint8_t* scales;
-  uint8_t* block_max;  // optional: largest scale byte of each (128-row block, head)
+  uint8_t* group_max;  // optional: largest scale byte of each (16-row group, head)
 };
 
 struct CastParams {
@@ -48,7 +48,7 @@ struct AttnParams {
   uint16_t* out;
   float* lse;
   const uint8_t* k_end;
-  const uint8_t* k_bmax;  // optional per-(128-row scale block, head) maximum K scale byte  // one past the last byte of K / V: loads beyond read zeros
+  const uint8_t* k_gmax;  // optional per-(16-row scale group, head) maximum K scale byte  // one past the last byte of K / V: loads beyond read zeros
   const uint8_t* v_end;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;  // elements
   int64_t qd_ss, qd_sh, kd_ss, kd_sh, vd_ss, vd_sh;

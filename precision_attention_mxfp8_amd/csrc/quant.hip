@@ -6,15 +6,16 @@
 // FastVideo fp8-PV PR (unscaled e4m3 cast of V).
 //
 // Work mapping (HBM-bound, one pass over the input):
-//   A workgroup owns one (128-row block of the scale storage, head) pair: 16 rows per pass, 8
-//   passes. 16 lanes own one (scale row, head) pair = 128 elements; each lane loads 8
+//   A workgroup owns 16 consecutive rows of the scale storage for one head; 16 lanes own one
+//   (scale row, head) pair = 128 elements; each lane loads 8
 //   consecutive elements with one 16-byte load (two for FP32). The 4 lanes of a 32-element
 //   block reduce their maximum with two cross-lane xor steps inside a quad (DPP), derive the
 //   exponent from the maximum's bits, scale by an exact power of two and convert with the
 //   hardware E4M3 conversion (round to nearest even). Lane 0 of the 16 gathers the four scale
 //   bytes and writes them as one word. Pad rows of the scale storage get 0x7F and no payload.
-//   Optionally the workgroup also writes the largest scale byte of its block's real rows (one
-//   byte per block and head): the attention kernel's precision guard bounds |k| with it.
+//   Optionally the workgroup also writes the largest scale byte of its 16 rows' real rows (one
+//   byte per 16-row group and head, 0 for a group of pad rows only): the attention kernel's
+//   precision guard bounds |k| with it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,33 +71,25 @@ template <typename T>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
   __shared__ uint32_t red[4];
   const int h = (int)(blockIdx.x % (unsigned)p.num_heads);  // neighbouring workgroups: same rows
-  const int64_t blk = blockIdx.x / (unsigned)p.num_heads;
-  const int sub = threadIdx.x & 15;  // 8-element chunk of the 128-element row
-  const int64_t srow0 = blk * 128;
+  const int64_t grp16 = blockIdx.x / (unsigned)p.num_heads;  // 16-row group of the scale storage
+  const int sub = threadIdx.x & 15;                           // 8-element chunk of the 128-element row
+  const int64_t srow = grp16 * 16 + (threadIdx.x >> 4);
 
-  // sequence owning this block (every block lies inside one sequence's padded rows): the
-  // largest i with cu_scale[i] <= srow0
+  // sequence owning this group (groups never straddle sequences: each sequence's scale rows are
+  // padded to a multiple of 128): the largest i with cu_scale[i] <= srow
   int lo = 0, hi = p.num_seqs;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if ((int64_t)p.cu_scale[mid] <= srow0) lo = mid; else hi = mid;
+    if ((int64_t)p.cu_scale[mid] <= srow) lo = mid; else hi = mid;
   }
-  const int64_t local0 = srow0 - p.cu_scale[lo];
+  const int64_t local = srow - p.cu_scale[lo];
   const int64_t seq_len = (int64_t)p.cu_seqlens[lo + 1] - p.cu_seqlens[lo];
-  const int64_t t0 = p.cu_seqlens[lo] + local0;
-  const int base = (threadIdx.x & 63) & ~15;
-
+  uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
   uint32_t smax = 0;
-#pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int r = pass * 16 + (int)(threadIdx.x >> 4);  // row inside the block
-    const int64_t srow = srow0 + r;
-    uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
-    if (local0 + r >= seq_len) {  // pad row of the 128-token-padded scale storage
-      if (sub == 0) *scale_word = 0x7F7F7F7Fu;
-      continue;
-    }
-    const int64_t t = t0 + r;
+  if (local >= seq_len) {  // pad row of the 128-token-padded scale storage
+    if (sub == 0) *scale_word = 0x7F7F7F7Fu;
+  } else {
+    const int64_t t = p.cu_seqlens[lo] + local;
     float v[8];
     Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
     float amax = 0.0f;
@@ -115,20 +108,21 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
     // gather the 4 block scale bytes of this row into lane 0 of the 16 (all 16 lanes of a row
     // take this branch together: the row decides it)
     const uint32_t sbyte = (uint32_t)(e + 127);
-    smax = max(smax, sbyte);
+    smax = sbyte;
+    const int base = (threadIdx.x & 63) & ~15;
     uint32_t b1 = __shfl(sbyte, base + 4);
     uint32_t b2 = __shfl(sbyte, base + 8);
     uint32_t b3 = __shfl(sbyte, base + 12);
     if (sub == 0) *scale_word = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
   }
 
-  if (p.block_max != nullptr) {  // uniform over the workgroup
+  if (p.group_max != nullptr) {  // uniform over the workgroup
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) smax = max(smax, (uint32_t)__shfl_xor((int)smax, s));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = smax;
     __syncthreads();
     if (threadIdx.x == 0)
-      p.block_max[blk * p.num_heads + h] = (uint8_t)max(max(red[0], red[1]), max(red[2], red[3]));
+      p.group_max[grp16 * p.num_heads + h] = (uint8_t)max(max(red[0], red[1]), max(red[2], red[3]));
   }
 }
 
@@ -150,9 +144,9 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
 }  // namespace
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
-  const int64_t blocks = p.total_scale_rows / 128 * p.num_heads;  // scale rows: whole blocks
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks);
+  const int64_t groups = p.total_scale_rows / 16 * p.num_heads;  // scale rows: whole 128-row blocks
+  if (groups == 0) return hipSuccess;
+  const dim3 grid((unsigned)groups);
   if (p.x_dtype == LPFA_DTYPE_BF16)
     hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   else

@@ -385,8 +385,8 @@ def test_graph_replay_matches_eager(pv_mode):
 
 @pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
 @pytest.mark.parametrize("which", ["outliers", "dense"])
-def test_k_block_max_same_results(pv_mode, which):
-    """The precision guard takes the same decisions from the quantizer's K block maxima as from its
+def test_k_group_max_same_results(pv_mode, which):
+    """The precision guard takes the same decisions from the quantizer's K group maxima as from its
     own scan of the K scales: O and LSE are bit-identical with and without them. The outlier input
     mixes tiles on the FP8 and on the BF16 score path within one launch."""
     if which == "outliers":
@@ -398,16 +398,16 @@ def test_k_block_max_same_results(pv_mode, which):
     mk = lp.VarlenMeta.from_lengths(wl.lengths_k, dev)
     q = lp.quantize_mxfp8_varlen(bf16_to_device(wl.q_bits), mq)
     k = lp.quantize_mxfp8_varlen(bf16_to_device(wl.k_bits), mk)
-    assert k.block_max is not None
+    assert k.group_max is not None
     v = bf16_to_device(wl.v_bits)
     if pv_mode == "fp8":
         v = lp.cast_e4m3(v)
     o1, l1 = lp.lp_attn_varlen_fwd(q, k, v, mq, mk, pv_mode=pv_mode)
     o1, l1 = o1.clone(), l1.clone()
-    k_scan = lp.Mxfp8Tensor(k.payload, k.scales, mk)   # no block maxima: the kernel scans
+    k_scan = lp.Mxfp8Tensor(k.payload, k.scales, mk)   # no group maxima: the kernel scans
     o2, l2 = lp.lp_attn_varlen_fwd(q, k_scan, v, mq, mk, pv_mode=pv_mode)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     with pytest.raises(ValueError):
-        bad = lp.Mxfp8Tensor(k.payload, k.scales, mk, k.block_max[:1])
+        bad = lp.Mxfp8Tensor(k.payload, k.scales, mk, k.group_max[:1])
         lp.lp_attn_varlen_fwd(q, bad, v, mq, mk, pv_mode=pv_mode)

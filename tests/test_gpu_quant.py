@@ -162,8 +162,9 @@ def test_deterministic_repeat():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def _block_max_from_scales(scales: np.ndarray, lengths) -> np.ndarray:
-    """Largest scale byte of each (128-row scale block, head) over the block's real rows."""
+def _group_max_from_scales(scales: np.ndarray, lengths) -> np.ndarray:
+    """Largest scale byte of each (16-row group of the scale storage, head) over the group's real
+    rows, 0 for a group of pad rows only."""
     rows, h, _ = scales.shape
     valid = np.zeros(rows, dtype=bool)
     start = 0
@@ -171,15 +172,16 @@ def _block_max_from_scales(scales: np.ndarray, lengths) -> np.ndarray:
         valid[start:start + n] = True
         start += -(-n // 128) * 128
     masked = np.where(valid[:, None, None], scales, 0).astype(np.uint8)
-    return masked.reshape(rows // 128, 128, h, 4).max(axis=(1, 3))
+    return masked.reshape(rows // 16, 16, h, 4).max(axis=(1, 3))
 
 
 @pytest.mark.parametrize("mode", ["rceil", "floor"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_block_max(mode, dtype):
-    """The quantizer's per-(128-row block, head) maximum scale byte equals the maximum of the
-    oracle's scale bytes over the block's real rows (pad rows, which hold 0x7F, excluded), with
-    ragged lengths, empty sequences and block exponents that differ from block to block."""
+def test_group_max(mode, dtype):
+    """The quantizer's per-(16-row group, head) maximum scale byte equals the maximum of the
+    oracle's scale bytes over the group's real rows (pad rows, which hold 0x7F, excluded; 0 for a
+    group of pad rows only), with ragged lengths, empty sequences and block exponents that differ
+    from block to block."""
     rng = np.random.default_rng(12)
     lengths = [0, 300, 1, 128, 129, 0, 517]
     h = 3
@@ -198,21 +200,22 @@ def test_block_max(mode, dtype):
     cu = np.concatenate([[0], np.cumsum(lengths)])
     _, rs, _ = oracle.mx_quantize_varlen(xo, cu, mode)
     assert np.array_equal(mx.scales.cpu().numpy(), rs)
-    got = mx.block_max.cpu().numpy()
-    want = _block_max_from_scales(rs, lengths)
-    assert got.shape == want.shape == (meta.total_scale_rows // 128, h)
+    got = mx.group_max.cpu().numpy()
+    want = _group_max_from_scales(rs, lengths)
+    assert got.shape == want.shape == (meta.total_scale_rows // 16, h)
+    assert (want == 0).any()   # some groups hold pad rows only
     assert np.array_equal(got, want)
     # the maxima really differ across blocks and heads in this input
     assert len(np.unique(want)) > 3
 
 
-def test_block_max_optional():
-    """Without a block_max buffer the quantizer writes payload and scales only, bit-identically."""
+def test_group_max_optional():
+    """Without a group_max buffer the quantizer writes payload and scales only, bit-identically."""
     wl = make_custom([300, 77], [300, 77], heads=2, seed=13)
     x = bf16_to_device(wl.q_bits)
     meta = lp.VarlenMeta.from_lengths(wl.lengths_q, x.device)
     a = lp.quantize_mxfp8_varlen(x, meta)
     b = lp.quantize_mxfp8_varlen(x, meta, out=lp.Mxfp8Tensor(torch.empty_like(a.payload), torch.empty_like(a.scales), meta))
     torch.cuda.synchronize()
-    assert b.block_max is None
+    assert b.group_max is None
     assert torch.equal(a.payload, b.payload) and torch.equal(a.scales, b.scales)
