@@ -800,12 +800,12 @@ struct Attn {
   template <bool FAST>
   __device__ __forceinline__ void main_loop(int niter) {
     v4f s[8][2];
-    if (ng > 0 && grp == 0) {  // group 1 takes its first scores inside its first iteration
-      if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
-    }
-    __syncthreads();  // K buffer 0 is reused for blk(2)
     int j = 0;
     if constexpr (G == 1) {
+      if (ng > 0) {
+        if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
+      }
+      __syncthreads();  // K buffer 0 is reused for blk(2)
       // iteration j writes its probabilities to pa (j even) or pb (j odd) and reads the
       // previous block's from the other set
       PF pa, pb;
@@ -828,8 +828,20 @@ struct Attn {
       if (ng & 1) pv<0>(0, pa);
       else pv<1>(0, pb);
     } else {
-      // separate loops per group (the order of work differs), each register-allocated alone
-      if (grp == 0) loop2<0, FAST>(s, niter); else loop2<1, FAST>(s, niter);
+      // separate loops per group (the order of work differs), each register-allocated alone.
+      // Group 0 takes the scores of its first block here (group 1 inside its first iteration),
+      // inside its own branch so that no score tile is live across the split; one barrier each
+      // (K buffer 0 is reused for blk(2)).
+      if (grp == 0) {
+        if (ng > 0) {
+          if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
+        }
+        __syncthreads();
+        loop2<0, FAST>(s, niter);
+      } else {
+        __syncthreads();
+        loop2<1, FAST>(s, niter);
+      }
     }
   }
 
