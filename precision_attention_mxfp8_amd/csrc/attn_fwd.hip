@@ -80,6 +80,9 @@ constexpr float GUARD_LOG2 = 16.0f;
 // Stale-maximum slack of the online softmax, in log2 units: probabilities may be taken against
 // a maximum up to 8 below the running one (P <= 2^8).
 constexpr float LAZY_LOG2 = 8.0f;
+// Two-group softmax: largest sum of one lane's probabilities of a row taken against a stale
+// maximum (it bounds each of them, as LAZY_LOG2 does for the one-group kernel)
+constexpr float LAZY_SUM = 256.0f;
 
 template <bool FP8V>
 struct Groups { static constexpr int G = FP8V ? 2 : 1; };
@@ -546,12 +549,40 @@ struct Attn {
   }
 
   // ---------------------------------------------------------------- two-group phases
-  // Softmax of key block b (scores in s): mask, lazy running maximum, O and the rounded sum
-  // rescaled at once when the maximum moves (O holds exactly the P V of the earlier blocks
-  // here), probabilities -> pf, unrounded row sums -> l_run.
-  template <bool MASK>
-  __device__ __forceinline__ void softmax(int b, v4f s[8][2], PF& pf) {
-    if (MASK) {
+  // Probabilities of key block (scores in s) against the running maximum m_run: pf <- the packed
+  // probabilities, rs <- this lane's unrounded sums over its keys of each row.
+  __device__ __forceinline__ void probs(const v4f s[8][2], PF& pf, float rs[2]) const {
+    rs[0] = rs[1] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pk[i] = __builtin_amdgcn_exp2f(fmaf(s[k][nt][i], c, -m_run[nt]));
+          rs[nt] += pk[i];
+        }
+        if constexpr (FP8V) {
+          pf.f8[nt][k] = (int)cvt4_e4m3_over((uint32_t)pf.f8[nt][k], pk[0], pk[1], pk[2], pk[3]);
+        } else {
+          pf.w[k >> 1][nt][2 * (k & 1)] = cvt_pk_bf16(pk[0], pk[1]);
+          pf.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(pk[2], pk[3]);
+        }
+      }
+    }
+  }
+
+  // Softmax of key block b (scores in s): mask, lazy running maximum, probabilities -> pf,
+  // unrounded row sums -> l_run. The maximum is only taken when needed: the probabilities are
+  // first formed against the current m_run, and each lane's sum over its keys of a row bounds
+  // every probability it holds, so when no such sum exceeds 2^8 none of them does and the block
+  // is done. Otherwise (and on the wave's first block, when m_run is still -inf) the block's row
+  // maxima move m_run, O and the rounded sum are rescaled at once (O holds exactly the P V of the
+  // earlier blocks here), and the probabilities are formed again.
+  template <bool FIRST>
+  __device__ __forceinline__ void softmax(int b, bool mask, v4f s[8][2], PF& pf) {
+    if (mask) {  // wave-uniform: the block runs past the last key
       const int kb = b * BN;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
@@ -562,50 +593,28 @@ struct Attn {
             s[mt][1][i] = -INFINITY;
           }
     }
-    float cand[2];
-    bool move = false;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = fmaxf(s[0][nt][0], s[0][nt][1]);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(s[mt][nt][i], s[mt][nt][i + 1]));
-      mx = xmax16_32(mx);
-      cand[nt] = mx * c;
-      move = move || (cand[nt] > m_run[nt] + LAZY_LOG2);
+    float rs[2];
+    bool exact = FIRST;
+    if (!FIRST) {
+      probs(s, pf, rs);
+      exact = __ballot(!(rs[0] <= LAZY_SUM) || !(rs[1] <= LAZY_SUM)) != 0;  // wave-uniform
     }
-    if (__ballot(move) != 0) {  // wave-uniform, rare after the first block
-      const bool first = m_run[0] == -INFINITY;
+    if (exact) {
       float alpha[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float m_new = fmaxf(m_run[nt], cand[nt]);
+        float mx = fmaxf(s[0][nt][0], s[0][nt][1]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) mx = fmaxf(mx, fmaxf(s[mt][nt][i], s[mt][nt][i + 1]));
+        const float m_new = fmaxf(m_run[nt], xmax16_32(mx) * c);
         alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
         l_run[nt] *= alpha[nt];
         m_run[nt] = m_new;
       }
-      if (!first) rescale(alpha);
-    }
-    const float m_use[2] = {m_run[0], m_run[1]};
-    float rs[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pk[i] = __builtin_amdgcn_exp2f(fmaf(s[k][nt][i], c, -m_use[nt]));
-          rs[nt] += pk[i];
-        }
-        if constexpr (FP8V) {
-          pf.f8[nt][k] = (int)cvt4_e4m3(pk[0], pk[1], pk[2], pk[3]);
-        } else {
-          pf.w[k >> 1][nt][2 * (k & 1)] = cvt_pk_bf16(pk[0], pk[1]);
-          pf.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(pk[2], pk[3]);
-        }
-      }
+      if (!FIRST) rescale(alpha);
+      probs(s, pf, rs);
     }
     l_run[0] += rs[0];
     l_run[1] += rs[1];
@@ -773,12 +782,14 @@ struct Attn {
   // score phase). Targets: group 0's K(j+2) -> its K buffer j%2 and V(j+1) -> its V buffer
   // (j+1)%2; group 1's K(j+1) -> (j+1)%2 and V(j) -> j%2: each was last read in the previous
   // iteration. Every iteration ends with its loads complete and one barrier.
-  template <int GRP, bool FAST, bool FIRST, bool LAST>
+  template <int GRP, bool FAST, bool FIRST>
   __device__ __forceinline__ void iteration2(int j, v4f s[8][2], PF& pf) {
+    const bool last = j == ng - 1;
+    const bool mask = last && (Lk & (BN - 1)) != 0;
     if constexpr (GRP == 0) {
-      softmax<LAST>(blk(j), s, pf);
+      softmax<FIRST>(blk(j), mask, s, pf);
       pv<0>(j & 1, pf);
-      if (!LAST) {
+      if (!last) {
         if (FAST) qk((j + 1) & 1, s); else scores_bf16((j + 1) & 1, s);
       }
     } else {
@@ -789,7 +800,7 @@ struct Attn {
       if (j + 1 < ng0) dma_v(0, 2 * (j + 1), (j + 1) & 1);
       if (j + 1 < ng) dma_k(1, 2 * (j + 1) + 1, (j + 1) & 1);
       dma_v(1, 2 * j + 1, j & 1);
-      softmax<LAST>(blk(j), s, pf);
+      softmax<FIRST>(blk(j), mask, s, pf);
     }
     wait_vm_all();
     __syncthreads();
@@ -847,16 +858,11 @@ struct Attn {
 
   template <int GRP, bool FAST>
   __device__ __forceinline__ void loop2(v4f s[8][2], int niter) {
-    PF pf;
+    PF pf{};  // defined contents: the packing writes over the previous probabilities
     int j = 0;
-    if (ng == 1) {
-      iteration2<GRP, FAST, true, true>(0, s, pf);
-      j = 1;
-    } else if (ng > 1) {
-      iteration2<GRP, FAST, true, false>(0, s, pf);
-      for (j = 1; j < ng - 1; ++j) iteration2<GRP, FAST, false, false>(j, s, pf);
-      iteration2<GRP, FAST, false, true>(ng - 1, s, pf);
-      j = ng;
+    if (ng > 0) {
+      iteration2<GRP, FAST, true>(0, s, pf);
+      for (j = 1; j < ng; ++j) iteration2<GRP, FAST, false>(j, s, pf);
     }
     // group 1 still owes the P V of its last block: in the spare iteration if there is one
     bool owed = GRP == 1 && ng > 0;

@@ -25,6 +25,14 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
   return (uint32_t)w;
 }
 
+// The same four codes written over a register's old contents: both halves are replaced, so the
+// result does not depend on `old`, and no zeroing instruction precedes the first conversion.
+__device__ __forceinline__ uint32_t cvt4_e4m3_over(uint32_t old, float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
 // Two floats -> two BF16 (round to nearest even) packed in one word, first in the low half.
