@@ -792,14 +792,13 @@ struct Attn {
       if (!last) {
         if (FAST) qk((j + 1) & 1, s); else scores_bf16((j + 1) & 1, s);
       }
+      if (j + 2 < ng) dma_k(0, blk(j + 2), j & 1);
+      if (j + 1 < ng) dma_v(0, blk(j + 1), (j + 1) & 1);
     } else {
       if (!FIRST) pv<1>((j + 1) & 1, pf);
       if (FAST) qk(j & 1, s); else scores_bf16(j & 1, s);
-      const int ng0 = ng + (nb & 1);  // group 0 has the extra block when nb is odd
-      if (j + 2 < ng0) dma_k(0, 2 * (j + 2), j & 1);
-      if (j + 1 < ng0) dma_v(0, 2 * (j + 1), (j + 1) & 1);
-      if (j + 1 < ng) dma_k(1, 2 * (j + 1) + 1, (j + 1) & 1);
-      dma_v(1, 2 * j + 1, j & 1);
+      if (j + 1 < ng) dma_k(1, blk(j + 1), (j + 1) & 1);
+      dma_v(1, blk(j), j & 1);
       softmax<FIRST>(blk(j), mask, s, pf);
     }
     wait_vm_all();
