@@ -207,6 +207,8 @@ struct Attn {
   uint32_t lds_base;         // the same, as an LDS byte address
   LDS uint8_t* vobj[2];      // the two static V objects; always indexed by constants
   int seq, head, H, Lk, nb;
+  int q_start, Lq, k_start;  // the sequence's first query and key rows, and its query count
+  int scq, sck;              // its first scale rows (MX mode)
   int lane, wave, n16, g;    // wave: index inside the group (queries 32*wave ..)
   int grp, ng;               // wave group, and the number of key blocks it processes
   const uint8_t* kbase;      // key row 0 of this (sequence, head)
@@ -328,13 +330,35 @@ struct Attn {
   __device__ __forceinline__ uint32_t guard_elem(int i) const {
     return kgm_base ? (uint32_t)kgm_base[(int64_t)i * H] : *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)i * H * 4);
   }
+  // Branch-free, so that the eight loads go out together: an index past the end reads the last
+  // element again, which leaves the maximum unchanged (and the values are not used before the
+  // reduction, so nothing waits for them here).
   __device__ __forceinline__ void guard_prefetch() {
     const int n = guard_count();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = (int)threadIdx.x + u * 256 * G;
-      ksw[u] = i < n ? guard_elem(i) : 0u;
+    for (int u = 0; u < 8; ++u) ksw[u] = 0u;
+    if (n == 0) return;
+    if (kgm_base) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        ksw[u] = kgm_base[(int64_t)min((int)threadIdx.x + u * 256 * G, n - 1) * H];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        ksw[u] = *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)min((int)threadIdx.x + u * 256 * G, n - 1) * H * 4);
     }
+  }
+
+  // The sequence's offsets, loaded together (one memory round trip) and kept in scalar registers.
+  __device__ __forceinline__ void load_meta() {
+    const int q0 = p.cu_q[seq], q1 = p.cu_q[seq + 1], k0 = p.cu_k[seq], k1 = p.cu_k[seq + 1];
+    const int sq = MX ? p.cu_scale_q[seq] : 0, sk = MX ? p.cu_scale_k[seq] : 0;
+    q_start = __builtin_amdgcn_readfirstlane(q0);
+    Lq = __builtin_amdgcn_readfirstlane(q1) - q_start;
+    k_start = __builtin_amdgcn_readfirstlane(k0);
+    Lk = __builtin_amdgcn_readfirstlane(k1) - k_start;
+    scq = __builtin_amdgcn_readfirstlane(sq);
+    sck = __builtin_amdgcn_readfirstlane(sk);
   }
 
   __device__ __forceinline__ void guard_publish(float* red) {
@@ -884,11 +908,7 @@ struct Attn {
     constexpr bool GUARD = MODE != 1;     // this call evaluates the guard
     constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
     H = p.num_heads;
-    const int q_start = p.cu_q[seq];
-    const int Lq = p.cu_q[seq + 1] - q_start;
     const int q0 = qtile * BM;
-    const int k_start = p.cu_k[seq];
-    Lk = p.cu_k[seq + 1] - k_start;
     nb = (Lk + BN - 1) / BN;
     ng = (nb - grp + G - 1) / G;
     const int niter = (nb + G - 1) / G;
@@ -908,8 +928,8 @@ struct Attn {
     vbase = reinterpret_cast<const uint8_t*>(p.v) + ((int64_t)k_start * p.v_st + (int64_t)head * p.v_sh) * (FP8V ? 1 : 2);
     k_st_b = p.k_st;
     v_st_b = p.v_st * (FP8V ? 1 : 2);
-    ksc_base = MX ? p.k_scale + ((int64_t)p.cu_scale_k[seq] * H + head) * 4 : nullptr;
-    kgm_base = MX && p.k_gmax ? p.k_gmax + (int64_t)(p.cu_scale_k[seq] / 16) * H + head : nullptr;
+    ksc_base = MX ? p.k_scale + ((int64_t)sck * H + head) * 4 : nullptr;
+    kgm_base = MX && p.k_gmax ? p.k_gmax + (int64_t)(sck / 16) * H + head : nullptr;
     if (MX && GUARD) guard_prefetch();
 
     // start the first loads before touching Q
@@ -924,37 +944,36 @@ struct Attn {
     }
 
     // ---- Q fragments: FP8 (score B operand); the guarded path reloads them as BF16 ----
+    // Branch-free: a row past the sequence's end reads its last row (the tile has at least one)
+    // and is then zeroed, so that every load goes out at once.
     uint32_t qmax_code = 0, qmax_scale = 0;
     v8i qf[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int qi = q0 + wave * 32 + nt * 16 + n16;
-      if (qi < Lq) {
-        const uint8_t* qp = p.q + (int64_t)(q_start + qi) * p.q_st + (int64_t)head * p.q_sh;
-        const uint4 a = ldg16(qp + 16 * g), b = ldg16(qp + 64 + 16 * g);
-        qf[nt] = make_v8i(a, b);
-        const uint32_t sw = MX ? *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)p.cu_scale_q[seq] + qi) * H + head) * 4)
-                               : 0x7F7F7F7Fu;
-        qsc[nt] = (int)((sw >> (8 * g)) & 0xFFu);
-        if (MAY_SLOW) {
-          qrow[nt] = qp;
-          qsw[nt] = sw;
-        }
-        uint32_t words[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w = words[i] & 0x7F7F7F7Fu;
-          qmax_code = max(qmax_code, max(max(w & 0xFF, (w >> 8) & 0xFF), max((w >> 16) & 0xFF, w >> 24)));
-        }
-        qmax_scale = max(qmax_scale, (uint32_t)qsc[nt]);
-      } else {
-        qf[nt] = make_v8i(make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0));
-        qsc[nt] = 127;
-        if (MAY_SLOW) {
-          qrow[nt] = nullptr;
-          qsw[nt] = 0x7F7F7F7Fu;
-        }
+      const bool in = qi < Lq;
+      const int qc = in ? qi : Lq - 1;
+      const uint8_t* qp = p.q + (int64_t)(q_start + qc) * p.q_st + (int64_t)head * p.q_sh;
+      uint4 a = ldg16(qp + 16 * g), b = ldg16(qp + 64 + 16 * g);
+      uint32_t sw = MX ? *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)scq + qc) * H + head) * 4) : 0x7F7F7F7Fu;
+      if (!in) {
+        a = make_uint4(0, 0, 0, 0);
+        b = make_uint4(0, 0, 0, 0);
+        sw = 0x7F7F7F7Fu;
       }
+      qf[nt] = make_v8i(a, b);
+      qsc[nt] = (int)((sw >> (8 * g)) & 0xFFu);
+      if (MAY_SLOW) {
+        qrow[nt] = in ? qp : nullptr;
+        qsw[nt] = sw;
+      }
+      uint32_t words[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w = words[i] & 0x7F7F7F7Fu;
+        qmax_code = max(qmax_code, max(max(w & 0xFF, (w >> 8) & 0xFF), max((w >> 16) & 0xFF, w >> 24)));
+      }
+      qmax_scale = max(qmax_scale, in ? (uint32_t)qsc[nt] : 0u);
     }
     if (grp == 0) {  // both groups hold the same queries: group 0 stores the fragments
       LDS v4u_t* qa = lds_at<v4u_t>(lds_base + L::OFF_Q + wave * 2 * 2048 + lane * 16);
@@ -1075,6 +1094,7 @@ __device__ __attribute__((noinline)) void slow_tile(const AttnParams* pp, uint8_
   Attn<MX, FP8V> a(p, smem, __builtin_amdgcn_readfirstlane(grp), va, vb);
   a.seq = __builtin_amdgcn_readfirstlane(seq);
   a.head = __builtin_amdgcn_readfirstlane(head);
+  a.load_meta();
   a.template run<1>(__builtin_amdgcn_readfirstlane(qtile));
 }
 
@@ -1096,13 +1116,14 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
     head = rest % p.num_heads;
     seq = rest / p.num_heads;
   }
-  if (qtile * BM >= p.cu_q[seq + 1] - p.cu_q[seq]) return;
   __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V>::VOBJ_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V>::VOBJ_BYTES];
   const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
   Attn<MX, FP8V> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
   a.seq = seq;
   a.head = head;
+  a.load_meta();
+  if (qtile * BM >= a.Lq) return;
   if constexpr (Groups<FP8V>::G == 1) {
     a.template run<2>(qtile);  // 512 registers per wave: both score loops fit in one allocation
   } else if (!a.template run<0>(qtile)) {
