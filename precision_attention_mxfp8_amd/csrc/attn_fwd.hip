@@ -106,11 +106,12 @@ struct Lay {
   // in flight into K never hold up the transposing V reads (the compiler makes those reads wait
   // for every outstanding load into the same object). One group: object i is V buffer i. Two
   // groups: object g holds group g's two V buffers, and each group issues its V loads only
-  // after its own V reads of the iteration. The merge of the two groups reuses the objects
-  // (16 v4f per lane per wave of group 1) plus 2 v4f per lane per wave of the K area.
+  // after its own V reads of the iteration. The merge of the two groups passes half of each
+  // group's O (8 v4f per lane per wave) through the group's K buffers and its (m, l, rounded
+  // sum) (2 v4f per lane per wave) through half of the Q area.
   static constexpr int VOBJ_BYTES = 32768;
   static_assert(V_BYTES * Groups<FP8V>::G == VOBJ_BYTES, "V objects");
-  static_assert(Groups<FP8V>::G == 1 || (16 * 64 * 16 <= VOBJ_BYTES / 2 && 4 * 2 * 64 * 16 <= OFF_RED), "merge area");
+  static_assert(Groups<FP8V>::G == 1 || (4 * 8 * 64 * 16 <= 2 * K_BYTES && 2 * 4 * 2 * 64 * 16 <= 4 * 2 * 2048), "merge area");
 };
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
@@ -208,6 +209,7 @@ struct Attn {
   LDS uint8_t* vobj[2];      // the two static V objects; always indexed by constants
   int seq, head, H, Lk, nb;
   int q_start, Lq, k_start;  // the sequence's first query and key rows, and its query count
+  int qtile0;                // this tile's index among the sequence's query tiles
   int scq, sck;              // its first scale rows (MX mode)
   int lane, wave, n16, g;    // wave: index inside the group (queries 32*wave ..)
   int grp, ng;               // wave group, and the number of key blocks it processes
@@ -899,6 +901,73 @@ struct Attn {
     if (owed) pv<GRP>((ng - 1) & 1, pf);
   }
 
+  // ---------------------------------------------------------------- end of the tile
+  // d tiles DT0..DT0+3 of O (both query halves) into the LDS area at `give` (lane-contiguous
+  // 16-byte slots, 8 per lane).
+  template <int DT0>
+  __device__ __forceinline__ void give_half(LDS v4f* give) const {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) give[(2 * d + nt) * 64] = o[DT0 + d][nt];
+  }
+
+  // Combines this group's state with the other group's (m, l, rounded sum) in ml/os and its
+  // half of O at `take` (d tiles 0-3 for group 0, 4-7 for group 1). Every sum takes group 0's
+  // term first, so both groups compute the same l, rounded sum and m.
+  template <int GRP>
+  __device__ __forceinline__ void merge_half(const LDS v4f* take, const v4f ml, const v4f os) {
+    float aw[2], at[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float m = fmaxf(m_run[nt], ml[nt]);      // finite: group 0 has at least one block
+      aw[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m);
+      at[nt] = __builtin_amdgcn_exp2f(ml[nt] - m);   // 0 for a group with no block (-inf)
+      const float w0 = GRP == 0 ? aw[nt] : at[nt], w1 = GRP == 0 ? at[nt] : aw[nt];
+      const float l0 = GRP == 0 ? l_run[nt] : ml[2 + nt], l1 = GRP == 0 ? ml[2 + nt] : l_run[nt];
+      const float s0 = GRP == 0 ? o_sum[nt][0] : os[nt], s1 = GRP == 0 ? os[nt] : o_sum[nt][0];
+      l_run[nt] = l0 * w0 + l1 * w1;
+      o_sum[nt][0] = s0 * w0 + s1 * w1;
+      m_run[nt] = m;
+    }
+    constexpr int DT0 = GRP == 0 ? 0 : 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const v4f t = take[(2 * d + nt) * 64];
+        o[DT0 + d][nt] = GRP == 0 ? o[DT0 + d][nt] * aw[nt] + t * at[nt] : t * at[nt] + o[DT0 + d][nt] * aw[nt];
+      }
+  }
+
+  // O d tiles DT0..DT1-1 = O^T / (rounded sum) * vd -> BF16; with LSE, also
+  // LSE = ln2 * (m + log2 l).
+  template <int DT0, int DT1>
+  __device__ __forceinline__ void epilogue(float vd, bool with_lse) {
+    const int q0 = qtile0 * BM;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float lt = l_run[nt] + __shfl_xor(l_run[nt], 16);
+      lt += __shfl_xor(lt, 32);
+      const int qi = q0 + wave * 32 + nt * 16 + n16;
+      if (qi < Lq) {
+        const float ls = o_sum[nt][0];  // every row of the ones tile holds the rounded sum
+        const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+        uint16_t* op = p.out + ((int64_t)(q_start + qi) * H + head) * 128 + 4 * g;
+#pragma unroll
+        for (int dt = DT0; dt < DT1; ++dt) {
+          const v4f x = o[dt][nt];
+          const uint2 w = make_uint2(cvt_pk_bf16((x[0] * inv) * vd, (x[1] * inv) * vd),
+                                     cvt_pk_bf16((x[2] * inv) * vd, (x[3] * inv) * vd));
+          *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+        }
+        if (with_lse && g == 0)
+          p.lse[(int64_t)head * p.total_q + q_start + qi] =
+              lt > 0.0f ? (m_run[nt] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+      }
+    }
+  }
+
   // One query tile. The precision guard decides before the key loop between FP8 and BF16
   // scores. MODE 2: both loops in this function. MODE 0: FP8 scores only; when the guard fails,
   // every wave returns false with no load in flight and nothing written, and the caller runs the
@@ -908,6 +977,7 @@ struct Attn {
     constexpr bool GUARD = MODE != 1;     // this call evaluates the guard
     constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
     H = p.num_heads;
+    qtile0 = qtile;
     const int q0 = qtile * BM;
     nb = (Lk + BN - 1) / BN;
     ng = (nb - grp + G - 1) / G;
@@ -1014,67 +1084,36 @@ struct Attn {
       }
     }
 
-    if (G == 2) {
-      if (nb > 0) {
-        // Merge the two groups' partial results: group 1 leaves (m, l, O, rounded sum) in LDS,
-        // group 0 takes m = max(m0, m1) and adds each part scaled by 2^(m_g - m).
-        LDS v4f* area = reinterpret_cast<LDS v4f*>((wave < 2 ? vobj[0] : vobj[1]) + (wave & 1) * (L::VOBJ_BYTES / 2)) + lane;
-        LDS v4f* extra = reinterpret_cast<LDS v4f*>(LDS_PTR(uint8_t, lds - grp * L::GROUP_BYTES)) + wave * 2 * 64 + lane;
-        __syncthreads();  // every buffer read of the main loop is done
-        if (grp == 1) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) area[(2 * dt + nt) * 64] = o[dt][nt];
-          extra[0] = v4f{m_run[0], m_run[1], l_run[0], l_run[1]};
-          extra[64] = v4f{o_sum[0][0], o_sum[1][0], 0.0f, 0.0f};
-        }
-        __syncthreads();
-        if (grp == 1) return true;
-        const v4f ml = extra[0];
-        const v4f os = extra[64];
-        float a0[2], a1[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float m = fmaxf(m_run[nt], ml[nt]);     // finite: group 0 has at least one block
-          a0[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m);
-          a1[nt] = __builtin_amdgcn_exp2f(ml[nt] - m);  // 0 when group 1 had no block (-inf)
-          l_run[nt] = l_run[nt] * a0[nt] + ml[2 + nt] * a1[nt];
-          o_sum[nt][0] = o_sum[nt][0] * a0[nt] + os[nt] * a1[nt];
-          m_run[nt] = m;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) o[dt][nt] = o[dt][nt] * a0[nt] + area[(2 * dt + nt) * 64] * a1[nt];
-      } else if (grp == 1) {
-        return true;
-      }
-    }
-
-    // ---- epilogue: O = O^T / (rounded sum) * vd -> BF16; LSE = ln2 * (m + log2 l) ----
     const float vd = p.v_descale ? p.v_descale[seq * p.vd_ss + head * p.vd_sh] : 1.0f;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float lt = l_run[nt] + __shfl_xor(l_run[nt], 16);
-      lt += __shfl_xor(lt, 32);
-      const int qi = q0 + wave * 32 + nt * 16 + n16;
-      if (qi < Lq) {
-        const float ls = o_sum[nt][0];  // every row of the ones tile holds the rounded sum
-        const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
-        uint16_t* op = p.out + ((int64_t)(q_start + qi) * H + head) * 128 + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const v4f x = o[dt][nt];
-          const uint2 w = make_uint2(cvt_pk_bf16((x[0] * inv) * vd, (x[1] * inv) * vd),
-                                     cvt_pk_bf16((x[2] * inv) * vd, (x[3] * inv) * vd));
-          *reinterpret_cast<uint2*>(op + 16 * dt) = w;
-        }
-        if (g == 0)
-          p.lse[(int64_t)head * p.total_q + q_start + qi] =
-              lt > 0.0f ? (m_run[nt] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+    if (G == 2 && nb > 0) {
+      // Merge of the two groups' partial results, split by d tile: group 0 finishes d tiles 0-3,
+      // group 1 d tiles 4-7. Each group passes the other half of its O and its (m, l, rounded
+      // sum) through its own K area and a slice of the Q area, which the key loop no longer
+      // reads, so one barrier suffices; both then take m = max(m0, m1) and add the two parts
+      // scaled by 2^(m_g - m), and store their own half.
+      const uint32_t dyn0 = lds_base - grp * L::GROUP_BYTES;  // start of the dynamic area
+      LDS v4f* give = lds_at<v4f>(lds_base + L::OFF_K) + wave * 8 * 64 + lane;
+      LDS v4f* take = lds_at<v4f>(dyn0 + (1 - grp) * L::GROUP_BYTES + L::OFF_K) + wave * 8 * 64 + lane;
+      LDS v4f* xgive = lds_at<v4f>(dyn0 + L::OFF_Q + grp * 8192) + wave * 2 * 64 + lane;
+      LDS v4f* xtake = lds_at<v4f>(dyn0 + L::OFF_Q + (1 - grp) * 8192) + wave * 2 * 64 + lane;
+      if (grp == 0)
+        give_half<4>(give);
+      else
+        give_half<0>(give);
+      xgive[0] = v4f{m_run[0], m_run[1], l_run[0], l_run[1]};
+      xgive[64] = v4f{o_sum[0][0], o_sum[1][0], 0.0f, 0.0f};
+      __syncthreads();
+      if (grp == 0) {
+        merge_half<0>(take, xtake[0], xtake[64]);
+        epilogue<0, 4>(vd, true);
+      } else {
+        merge_half<1>(take, xtake[0], xtake[64]);
+        epilogue<4, 8>(vd, false);
       }
+      return true;
     }
+    if (G == 2 && grp == 1) return true;  // no key block: group 0 writes zeros and -inf
+    epilogue<0, 8>(vd, true);
     return true;
   }
 };
