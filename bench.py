@@ -308,8 +308,8 @@ def cpu_baseline(wl, pv_mode, rows_per_head, per_tensor):
     sample_flops = sum(4 * len(rows[r]) * wl.lengths_k[r] * wl.num_heads * 128 for r in rows)
     return {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(threads, cores)),
             "kind": "oracle",
-            "sample": f"float64 NumPy oracle: full MXFP8 quantize of Q and K, then attention for {rows_per_head} "
-                      f"query rows per (sequence, head) against all keys ({sample_flops / 1e9:.2f} GFLOP); "
+            "sample": f"float64 NumPy oracle: full MXFP8 quantize of Q and K, then attention for "
+                      f"{sum(len(v) for v in rows.values())} query rows of every head against all keys ({sample_flops / 1e9:.2f} GFLOP); "
                       f"{dt:.1f} s wall; host affinity {cores} cores"}
 
 
