@@ -30,12 +30,13 @@ encoder, brute force on tiny shapes); none is "parity unpinned".
 from .fp8 import (E4M3_MAX, E4M3_VALUES, e4m3_decode, e4m3_encode, e8m0_decode,
                   bf16_round, bf16_encode)
 from .mx import (padded_len, scale_offsets, mx_block_exponent, mx_quantize_varlen,
-                 mx_dequantize_varlen, e4m3_cast, pertensor_quantize)
+                 mx_dequantize_varlen, mx_quantize_varlen_tokens, mx_dequantize_varlen_tokens,
+                 e4m3_cast, pertensor_quantize)
 from .attention import attention_varlen, AttentionResult
 
 __all__ = [
     "E4M3_MAX", "E4M3_VALUES", "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round",
     "bf16_encode", "padded_len", "scale_offsets", "mx_block_exponent", "mx_quantize_varlen",
-    "mx_dequantize_varlen", "e4m3_cast", "pertensor_quantize", "attention_varlen",
+    "mx_dequantize_varlen", "mx_quantize_varlen_tokens", "mx_dequantize_varlen_tokens", "e4m3_cast", "pertensor_quantize", "attention_varlen",
     "AttentionResult",
 ]

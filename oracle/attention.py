@@ -10,7 +10,7 @@ optional per-tensor q/k/v descales, a missing one reading as 1.0):
     m_i   = max_j s_ij                      (the final row maximum: plain two-pass softmax)
     u_ij  = exp(s_ij - m_i)
     l_i   = sum_j u_ij                      (unrounded)
-    P_ij  = round_pv(u_ij)                  (BF16 in the bf16 mode, E4M3 unscaled in the fp8 mode)
+    P_ij  = round_pv(u_ij)                  (BF16 in the bf16 mode, E4M3 unscaled in the fp8 and mx modes)
     O_i   = vd * (sum_j P_ij V'_j) / l_i
     LSE_i = m_i + ln(l_i)                   (natural log of the sum of exp of the scaled scores)
 
@@ -21,8 +21,9 @@ lengths may differ. A sequence with queries but no keys has no defined output
 and is rejected.
 
 Qhat/Khat are the dequantized operands (MX payload times block scale, or the
-per-tensor payload), V' is the BF16 V (bf16 mode) or its E4M3 cast (fp8 mode),
-all passed in as float64.
+per-tensor payload), V' is the BF16 V (bf16 mode), its E4M3 cast (fp8 mode) or
+its dequantized token-orientation MXFP8 (mx mode: the LP-FA4 forward's v_mx
+operand, one scale per 32 tokens), all passed in as float64.
 """
 from __future__ import annotations
 
@@ -43,7 +44,8 @@ class AttentionResult:
 def _round_pv(u: np.ndarray, pv_mode: str) -> np.ndarray:
     if pv_mode == "bf16":
         return bf16_round(u)
-    if pv_mode == "fp8":
+    if pv_mode in ("fp8", "mx"):
+        # mx: V MXFP8 along tokens; the probabilities stay unscaled E4M3 as in the fp8 mode
         return e4m3_decode(e4m3_encode(u))
     raise ValueError(f"unknown pv_mode {pv_mode!r}")
 

@@ -112,6 +112,66 @@ def mx_dequantize_varlen(payload: np.ndarray, scales: np.ndarray, cu_seqlens: np
     return out.reshape(t, h, d)
 
 
+def mx_quantize_varlen_tokens(x: np.ndarray, cu_seqlens: np.ndarray, mode: str = "rceil"
+                              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Token-orientation MXFP8 of packed x (T, H, 128): one E8M0 scale per 32 consecutive tokens
+    of a sequence, per (head, d) — the orientation whose blocks run along the P V contraction.
+
+    LP-FA4 README, section "MXFP8 forward and backward": V is quantized by the same
+    routine as Q and K, and each tensor keeps both hardware orientations that the
+    forward and backward passes use. The P V product contracts over tokens, so its
+    V operand takes blocks of 32 along tokens.
+
+    Readings (the page gives no layout for this orientation):
+    * blocks start at each sequence's first token; the last block of a sequence may hold
+      fewer than 32 real tokens, and its maximum covers those only;
+    * exponent, scale byte and payload follow the same rules as the head_dim orientation
+      (``mx_block_exponent``; payload = E4M3(x * 2^-e), one rounding);
+    * scale layout: (sum_i P(L_i) / 32, H, 128) bytes; block b of sequence i sits at row
+      cu_scale[i] / 32 + b (cu_scale: prefix sums of P(L_i)); rows past a sequence's last
+      block hold 0x7F;
+    * the payload (T, H, 128) is packed like the input (no padding).
+    Returns (payload, scales, cu_scale).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 3:
+        raise ValueError("x must be (tokens, heads, head_dim)")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the method's domain")
+    t, h, d = x.shape
+    lengths = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu_seqlens[0] != 0 or cu_seqlens[-1] != t or np.any(lengths < 0):
+        raise ValueError("cu_seqlens must run from 0 to tokens, non-decreasing")
+    cu_scale = scale_offsets(lengths)
+    payload = np.zeros((t, h, d), dtype=np.uint8)
+    scales = np.full((int(cu_scale[-1]) // BLOCK, h, d), PAD_SCALE_BYTE, dtype=np.uint8)
+    for i, length in enumerate(lengths):
+        c0, row0 = int(cu_seqlens[i]), int(cu_scale[i]) // BLOCK
+        for b in range(-(-int(length) // BLOCK)):
+            lo, hi = c0 + BLOCK * b, c0 + min(BLOCK * (b + 1), int(length))
+            block = x[lo:hi]                                      # (<= 32 tokens, H, D)
+            e = mx_block_exponent(np.abs(block).max(axis=0), mode)   # (H, D)
+            payload[lo:hi] = e4m3_encode(block * np.ldexp(1.0, -e)[None])
+            scales[row0 + b] = (e + 127).astype(np.uint8)
+    return payload, scales, cu_scale
+
+
+def mx_dequantize_varlen_tokens(payload: np.ndarray, scales: np.ndarray, cu_seqlens: np.ndarray,
+                                cu_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """payload * 2^(scale - 127) with the scale of each token's 32-token block, float64 (T, H, 128)."""
+    t, h, d = payload.shape
+    lengths = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu_scale is None:
+        cu_scale = scale_offsets(lengths)
+    vals = e4m3_decode(payload)
+    out = np.empty_like(vals)
+    for i, length in enumerate(lengths):
+        c0, row0 = int(cu_seqlens[i]), int(cu_scale[i]) // BLOCK
+        for j in range(int(length)):
+            out[c0 + j] = vals[c0 + j] * e8m0_decode(scales[row0 + j // BLOCK])
+    return out
+
+
 def e4m3_cast(x: np.ndarray) -> np.ndarray:
     """Unscaled cast to E4M3 codes (the fp8 PV mode's V): round to nearest even, saturate at 448.
 
