@@ -256,23 +256,21 @@ struct Attn {
   // whose range ends at the tensor's last byte, so rows past the end of the last sequence
   // read zeros (rows past a sequence's end inside the tensor are other sequences' keys: masked
   // scores, zero probabilities). Each lane's 32-bit offsets are fixed for the whole sequence.
-  // K: instruction i of wave w fills 1 KB region R = 4w + i = key rows 8R..8R+7; lane L fetches
-  // row 8R + L/8, chunk (L%8) ^ (L/8). V fp8: same rows, chunk (L%8) ^ ((L/8)%4 | 4*(i/2)). V bf16:
-  // region R = 8w + i = rows 4R..4R+3 of 256 B; lane L fetches row 4R + L/16, chunk (L%16) ^ 2((L/16)%4).
+  // K: instruction i of wave w fills 1 KB region R = 4w + i = LDS rows 8R..8R+7; lane L fills
+  // row 8R + L/8 with chunk (L%8) ^ (L/8) of its key. V fp8: same rows, chunk (L%8) ^ ((L/8)%4 |
+  // 4*(i/2)). With E4M3 V the LDS rows hold the keys in the permuted order below (perm_base),
+  // else LDS row = key. V bf16: region R = 8w + i = rows 4R..4R+3 of 256 B; lane L fetches row
+  // 4R + L/16, chunk (L%16) ^ 2((L/16)%4).
   // K scales: waves 0 and 1 fetch 64 rows each, one 4-byte word per lane (the scale storage is
   // padded to whole blocks, so every row exists).
-  // The row step between a wave's instructions goes into a descriptor of its own (scalar
-  // work); each lane's offset is recomputed from its lane id at load time (a few integer
-  // instructions) rather than held in registers across the loop.
+  // The row step between a wave's instructions goes into the (uniform) instruction offset; each
+  // lane's offset is recomputed from its lane id at load time (a few integer instructions)
+  // rather than held in registers across the loop.
   __device__ __forceinline__ uint32_t k_off() const {
     const int r8 = lane >> 3;
     return (uint32_t)(r8 * (int)k_st_b) + 16u * ((lane & 7) ^ r8);
   }
-  __device__ __forceinline__ uint32_t v_off(int hi) const {
-    if (FP8V) {
-      const int r8 = lane >> 3;
-      return (uint32_t)(r8 * (int)v_st_b) + 16u * ((lane & 7) ^ ((r8 & 3) | (hi ? 4 : 0)));
-    }
+  __device__ __forceinline__ uint32_t v_off(int) const {  // BF16 V
     const int r4 = lane >> 4;
     return (uint32_t)(r4 * (int)v_st_b) + 16u * ((lane & 15) ^ (2 * (r4 & 3)));
   }
@@ -284,22 +282,44 @@ struct Attn {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
   }
 
+  // Key order in LDS for E4M3 V: LDS row 16t + 4g + i of a block holds key 32g + 4t + i
+  // (t = score tile, g = lane group, i = register). A score tile's lane group g then holds keys
+  // of the block's 32-key quarter g only, and so do the P V instruction's 32-slot groups (P is
+  // the B operand as the scores left it, and V's transposed reads follow the LDS rows): with V
+  // in MXFP8 along tokens, slot group g is exactly V's 32-token scale block g. For the rows one
+  // lane fills (LDS rows 32w + 8i + r, r = lane / 8, instruction i of wave w) the key is
+  // perm_base(r) + perm_step(i) with a lane part and a uniform per-instruction part.
+  __device__ __forceinline__ int perm_base(int r) const { return 32 * (r >> 2) + 8 * wave + (r & 3); }
+  __device__ __forceinline__ static int perm_step(int i) { return 64 * (i & 1) + 4 * (i >> 1); }
+
   // K block b into K buffer buf of wave group tg (the issuing wave's group may differ; tg is a
   // constant at every call).
   __device__ __forceinline__ void dma_k(int tg, int b, int buf) {
     uint8_t* area = lds + (tg - grp) * L::GROUP_BYTES;
-    const uint8_t* row0 = kbase + (int64_t)(b * BN + 32 * wave) * k_st_b;
     LDS uint8_t* dst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 4 * wave * 1024);
-    const uint32_t off = k_off();
-    const auto r = rsrc(row0, p.k_end);  // one descriptor per block; the row step goes into the offsets
+    if constexpr (FP8V) {
+      const int r8 = lane >> 3;
+      const uint32_t off = (uint32_t)(perm_base(r8) * (int)k_st_b) + 16u * ((lane & 7) ^ r8);
+      const auto r = rsrc(kbase + (int64_t)(b * BN) * k_st_b, p.k_end);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
-                                               off + (uint32_t)(8 * i) * (uint32_t)k_st_b, 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                                 off + (uint32_t)perm_step(i) * (uint32_t)k_st_b, 0, 0, 0);
+    } else {
+      const uint8_t* row0 = kbase + (int64_t)(b * BN + 32 * wave) * k_st_b;
+      const uint32_t off = k_off();
+      const auto r = rsrc(row0, p.k_end);  // one descriptor per block; the row step goes into the offsets
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                                 off + (uint32_t)(8 * i) * (uint32_t)k_st_b, 0, 0, 0);
+    }
     if (MX && wave < 2) {
-      const auto rs = rsrc(ksc_base + (int64_t)(b * BN + 64 * wave) * H * 4, ksc_base + (int64_t)(b * BN + BN) * H * 4);
+      // scale words of LDS rows 64w + L (w = 0, 1): key 32((L/4)%4) + 4(4w + L/16) + L%4 with E4M3 V
+      const int krow = FP8V ? 32 * ((lane >> 2) & 3) + 4 * (4 * wave + (lane >> 4)) + (lane & 3) : 64 * wave + lane;
+      const auto rs = rsrc(ksc_base + (int64_t)(b * BN) * H * 4, ksc_base + (int64_t)(b * BN + BN) * H * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(area + L::OFF_KSC + buf * L::KSC_BYTES + wave * 256), 4,
-                                               (uint32_t)(lane * H * 4), 0, 0, 0);
+                                               (uint32_t)(krow * H * 4), 0, 0, 0);
     }
   }
 
@@ -308,14 +328,24 @@ struct Attn {
     constexpr int N = FP8V ? 4 : 8;              // 1 KB regions per wave
     constexpr int ROWS = FP8V ? 8 : 4;           // key rows per region
     LDS uint8_t* dst = (obj == 0 ? vobj[0] : vobj[1]) + y * L::V_BYTES + N * wave * 1024;
-    const uint8_t* row0 = vbase + (int64_t)(b * BN + N * ROWS * wave) * v_st_b;
-    const uint32_t off0 = v_off(0), off1 = FP8V ? v_off(1) : off0;
-    const auto r = rsrc(row0, p.v_end);
+    if constexpr (FP8V) {  // rows in the permuted key order of dma_k
+      const int r8 = lane >> 3;
+      const uint32_t base = (uint32_t)(perm_base(r8) * (int)v_st_b);
+      const uint32_t off0 = base + 16u * ((lane & 7) ^ (r8 & 3)), off1 = base + 16u * ((lane & 7) ^ ((r8 & 3) | 4));
+      const auto r = rsrc(vbase + (int64_t)(b * BN) * v_st_b, p.v_end);
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
-                                               ((FP8V && (i & 2)) ? off1 : off0) + (uint32_t)(ROWS * i) * (uint32_t)v_st_b,
-                                               0, 0, 0);
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                                 ((i & 2) ? off1 : off0) + (uint32_t)perm_step(i) * (uint32_t)v_st_b, 0, 0, 0);
+    } else {
+      const uint8_t* row0 = vbase + (int64_t)(b * BN + N * ROWS * wave) * v_st_b;
+      const uint32_t off0 = v_off(0);
+      const auto r = rsrc(row0, p.v_end);
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
+                                                 off0 + (uint32_t)(ROWS * i) * (uint32_t)v_st_b, 0, 0, 0);
+    }
   }
 
   // ---------------------------------------------------------------- precision guard
@@ -614,7 +644,7 @@ struct Attn {
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (kb + 16 * mt + 4 * g + i >= Lk) {
+          if (kb + 32 * g + 4 * mt + i >= Lk) {  // the permuted key order of dma_k
             s[mt][0][i] = -INFINITY;
             s[mt][1][i] = -INFINITY;
           }
