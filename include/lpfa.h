@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 2
+#define LPFA_ABI_VERSION 3
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -56,6 +56,7 @@ extern "C" {
 
 #define LPFA_PV_BF16 0 /* V is BF16 (default mode, behaviour unchanged) */
 #define LPFA_PV_FP8 1  /* V is unscaled E4M3, implicit dequant scale 1.0 */
+#define LPFA_PV_MX 2   /* V is MXFP8 along tokens (mxfp8_quantize_varlen_tokens); P unscaled E4M3 */
 
 /* Version of this ABI (LPFA_ABI_VERSION of the built library). */
 int lpfa_abi_version(void);
@@ -102,6 +103,31 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
                           uint8_t* scales, uint8_t* group_max, void* stream);
 
 /*
+ * mxfp8_quantize_varlen_tokens - MXFP8 quantization along tokens (the P V operand's V).
+ * (LP-FA4 README, section "MXFP8 forward and backward": V is quantized like Q and K and
+ *  keeps both hardware orientations; the P V product contracts over tokens, so its V
+ *  operand takes blocks of 32 tokens.)
+ *
+ * For sequence i, head h, column d and 32-token block b of the sequence (tokens
+ * cu_seqlens[i] + 32b .. + 32b + 31, the last block of a sequence holding its real tokens
+ * only): amax = max |x| over the block's tokens; e, the scale byte e + 127 and
+ * payload[t, h, d] = E4M3(x * 2^-e) follow the rules of mxfp8_quantize_varlen.
+ *   scales[row, h, d] with row = cu_scale[i] / 32 + b; rows of a sequence past its last
+ *   block (up to P(L_i) / 32) are written as 0x7F.
+ *
+ *   x, strides, total_tokens, num_heads, head_dim, cu_seqlens, cu_scale, total_scale_rows,
+ *   scaling_mode: as in mxfp8_quantize_varlen (cu_scale: prefix sums of P(L_i)).
+ *   payload      output uint8 (T, num_heads, 128), contiguous.
+ *   scales       output uint8 (total_scale_rows / 32, num_heads, 128), contiguous.
+ * Errors: as mxfp8_quantize_varlen.
+ */
+int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                                 int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
+                                 int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
+                                 uint8_t* scales, void* stream);
+
+/*
  * lp_fp8_cast_e4m3 - unscaled E4M3 cast (the fp8 PV mode's V).
  * (FastVideo PR "fp8 PV mode for the FA4-FP4 attention path": an elementwise e4m3 cast
  *  of V with no scale factors; the attention reads it with dequant scale 1.0.)
@@ -138,7 +164,8 @@ typedef struct lpfa_attn_args {
   const int32_t* cu_scale_q; /* device int32[num_seqs + 1]; required with q_scale */
   const int32_t* cu_scale_k;
 
-  /* V: BF16 (pv_mode LPFA_PV_BF16) or E4M3 (LPFA_PV_FP8), (total_k, num_heads, 128). */
+  /* V: BF16 (pv_mode LPFA_PV_BF16), E4M3 (LPFA_PV_FP8) or the E4M3 payload of
+   * mxfp8_quantize_varlen_tokens (LPFA_PV_MX, with v_scale), (total_k, num_heads, 128). */
   const void* v;
   int64_t v_stride_tok, v_stride_head;
   int32_t pv_mode;
@@ -194,6 +221,11 @@ typedef struct lpfa_attn_args {
    * K bound there instead of scanning k_scale; the guard's decisions, and so the
    * results, are the same either way. Ignored in per-tensor mode. */
   const uint8_t* k_scale_group_max;
+
+  /* LPFA_PV_MX only (required there, else must be NULL): V's token-block scales from
+   * mxfp8_quantize_varlen_tokens, uint8 (cu_scale_k[num_seqs] / 32, num_heads, 128)
+   * contiguous; needs the MX mode (q_scale and k_scale set). */
+  const uint8_t* v_scale;
 } lpfa_attn_args;
 
 /*
@@ -205,9 +237,12 @@ typedef struct lpfa_attn_args {
  *   s_ij = softmax_scale * qd * kd * sum_b 2^(eq_ib + ek_jb) * sum_{d in b} q_id k_jd
  *   (eq, ek = 0 in per-tensor mode), running row max m and sum l over key blocks
  *   (online softmax), P rounded to V's type (BF16, or E4M3 with no scale), O_i =
- *   vd * (sum_j P_ij V_j) / l_i rounded to BF16, LSE_i = ln sum_j exp(s_ij).
+ *   vd * (sum_j P_ij V_j) / l_i rounded to BF16, LSE_i = ln sum_j exp(s_ij). In the
+ *   LPFA_PV_MX mode V_j = payload_j * 2^(ev) with ev the scale of token j's 32-token
+ *   block in each column.
  * Errors: LPFA_EINVAL (NULL pointers, bad strides/alignment, scale presence mismatch,
- * v_descale with BF16 V, bad pv_mode, struct_size too small, non-positive scale);
+ * v_descale with BF16 V, bad pv_mode, v_scale missing in (or given outside) the
+ * LPFA_PV_MX mode or without q_scale/k_scale, struct_size too small, non-positive scale);
  * LPFA_ENOTSUP (head_dim != 128, causal != 0); LPFA_EIO (launch failure).
  */
 int lp_attn_varlen_fwd(const lpfa_attn_args* args, void* stream);

@@ -1,12 +1,14 @@
 """MXFP8 attention forward for AMD Instinct MI355X (gfx950): HIP kernels behind a C ABI.
 
 Public API (marshalling only; the work runs in liblpfa.so):
-  VarlenMeta.from_lengths, quantize_mxfp8_varlen, cast_e4m3, lp_attn_varlen_fwd,
-  AttnPlan (a prepared lp_attn_varlen_fwd for repeated calls), longest_first_tile_order.
+  VarlenMeta.from_lengths, quantize_mxfp8_varlen, quantize_mxfp8_varlen_tokens, cast_e4m3,
+  lp_attn_varlen_fwd, AttnPlan (a prepared lp_attn_varlen_fwd for repeated calls),
+  longest_first_tile_order.
 """
-from .api import (AttnPlan, Mxfp8Tensor, VarlenMeta, cast_e4m3, longest_first_tile_order, lp_attn_varlen_fwd,
-                  quantize_mxfp8_varlen)
+from .api import (AttnPlan, Mxfp8Tensor, Mxfp8TokensTensor, VarlenMeta, cast_e4m3, longest_first_tile_order,
+                  lp_attn_varlen_fwd, quantize_mxfp8_varlen, quantize_mxfp8_varlen_tokens)
 from ._lib import LpfaError, load as load_library
 
-__all__ = ["AttnPlan", "Mxfp8Tensor", "VarlenMeta", "cast_e4m3", "longest_first_tile_order", "lp_attn_varlen_fwd",
-           "quantize_mxfp8_varlen", "LpfaError", "load_library"]
+__all__ = ["AttnPlan", "Mxfp8Tensor", "Mxfp8TokensTensor", "VarlenMeta", "cast_e4m3", "longest_first_tile_order",
+           "lp_attn_varlen_fwd", "quantize_mxfp8_varlen", "quantize_mxfp8_varlen_tokens", "LpfaError",
+           "load_library"]

@@ -19,10 +19,11 @@ LPFA_ENOTSUP = -95
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
-PV_MODES = {"bf16": 0, "fp8": 1}
+PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
+ABI_VERSION = 3
 
-EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "lp_fp8_cast_e4m3",
-           "lp_attn_varlen_fwd")
+EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
+           "lp_fp8_cast_e4m3", "lp_attn_varlen_fwd")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -56,6 +57,7 @@ class AttnArgs(ctypes.Structure):
         ("tile_order", _p), ("num_tiles", _i32),
         ("start_event", _p), ("stop_event", _p),
         ("k_scale_group_max", _p),
+        ("v_scale", _p),
     ]
 
 
@@ -90,6 +92,9 @@ def load() -> ctypes.CDLL:
         lib.mxfp8_quantize_varlen.restype = ctypes.c_int
         lib.mxfp8_quantize_varlen.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
                                               _i32, _i64, ctypes.c_int, _p, _p, _p, _p]
+        lib.mxfp8_quantize_varlen_tokens.restype = ctypes.c_int
+        lib.mxfp8_quantize_varlen_tokens.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
+                                                     _i32, _i64, ctypes.c_int, _p, _p, _p]
         lib.lp_fp8_cast_e4m3.restype = ctypes.c_int
         lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p]
         lib.lp_attn_varlen_fwd.restype = ctypes.c_int

@@ -99,6 +99,17 @@ class Mxfp8Tensor:
     group_max: Optional[torch.Tensor] = None
 
 
+@dataclass
+class Mxfp8TokensTensor:
+    """MXFP8 along tokens (V for the ``pv_mode="mx"`` P V product): E4M3 payload (T, H, 128) uint8
+    and E8M0 scales (sum P(L_i) / 32, H, 128) uint8, one per 32 consecutive tokens of a sequence
+    per (head, column); rows past a sequence's last 32-token block hold 0x7F."""
+
+    payload: torch.Tensor
+    scales: torch.Tensor
+    meta: VarlenMeta
+
+
 def _check_rows(x: torch.Tensor, name: str) -> None:
     if x.dim() != 3 or x.shape[2] != HEAD_DIM:
         raise ValueError(f"{name} must be (tokens, heads, {HEAD_DIM}), got {tuple(x.shape)}")
@@ -154,6 +165,37 @@ def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str =
         out.scales.data_ptr(), None if out.group_max is None else out.group_max.data_ptr(), _stream())
     if rc:
         _lib.check("mxfp8_quantize_varlen", rc)
+    return out
+
+
+def quantize_mxfp8_varlen_tokens(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str = "rceil",
+                                 out: Optional[Mxfp8TokensTensor] = None) -> Mxfp8TokensTensor:
+    """MXFP8-quantize packed (tokens, heads, 128) BF16/FP32 ``x`` along tokens (blocks of 32
+    consecutive tokens of a sequence, per head and column): the V operand of ``pv_mode="mx"``.
+
+    ``out``: an Mxfp8TokensTensor of the right shapes to write into; a new one otherwise."""
+    mode = _lib.SCALING.get(scaling_mode)
+    if mode is None:
+        raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
+    dt = _fp_input(x)
+    t, h, _ = x.shape
+    if t != meta.total_tokens:
+        raise ValueError(f"x has {t} tokens, metadata says {meta.total_tokens}")
+    sshape = (meta.total_scale_rows // 32, h, HEAD_DIM)
+    if out is None:
+        out = Mxfp8TokensTensor(torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device),
+                                torch.empty(sshape, dtype=torch.uint8, device=x.device), meta)
+    else:
+        _check_out(out.payload, (t, h, HEAD_DIM), torch.uint8, x.device, "out.payload")
+        _check_out(out.scales, sshape, torch.uint8, x.device, "out.scales")
+        if out.meta is not meta:
+            out = Mxfp8TokensTensor(out.payload, out.scales, meta)
+    rc = _lib.load().mxfp8_quantize_varlen_tokens(
+        x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM, meta.cu_seqlens.data_ptr(),
+        meta.cu_scale.data_ptr(), meta.num_seqs, meta.total_scale_rows, mode, out.payload.data_ptr(),
+        out.scales.data_ptr(), _stream())
+    if rc:
+        _lib.check("mxfp8_quantize_varlen_tokens", rc)
     return out
 
 
@@ -240,6 +282,8 @@ class AttnPlan:
                 raise ValueError("a sequence with queries must have at least one key")
         if meta_q.device != meta_k.device or meta_q.device.type != "cuda":
             raise ValueError("metadata must live on one GPU")
+        if pv_mode == "mx" and not mx:
+            raise ValueError("pv_mode='mx' needs MX (block-scaled) Q and K")
         h = int(num_heads)
         if h < 1:
             raise ValueError("num_heads must be positive")
@@ -324,6 +368,20 @@ class AttnPlan:
             qp, kp = q, k
         self._operand(qp, self._qshape, torch.uint8, "q")
         self._operand(kp, self._kshape, torch.uint8, "k")
+        if self.pv_mode == "mx":
+            if not isinstance(v, Mxfp8TokensTensor):
+                raise ValueError("pv_mode='mx' needs v as an Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
+            if v.meta is not self.meta_k and v.meta.cu_scale_host != self.meta_k.cu_scale_host:
+                raise ValueError("v was quantized with different sequence metadata")
+            vs, sshape = v.scales, (self.meta_k.total_scale_rows // 32, self.num_heads, HEAD_DIM)
+            if vs.shape != sshape or vs.dtype != torch.uint8 or not vs.is_contiguous() or vs.device != self._dev:
+                raise ValueError(f"v.scales must be a contiguous uint8 tensor of shape {sshape} on {self._dev}")
+            a.v_scale = vs.data_ptr()
+            v = v.payload
+        else:
+            if isinstance(v, Mxfp8TokensTensor):
+                raise ValueError("an Mxfp8TokensTensor V needs pv_mode='mx'")
+            a.v_scale = None
         self._operand(v, self._kshape, self._vdtype, "v")
         a.q, a.k, a.v = qp.data_ptr(), kp.data_ptr(), v.data_ptr()
         a.q_stride_tok, a.q_stride_head = qp.stride(0), qp.stride(1)
@@ -353,8 +411,8 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
     """Noncausal head_dim-128 attention forward over packed sequences -> (out BF16 (Tq,H,128), lse FP32 (H,Tq)).
 
     ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T) or raw E4M3 codes (per-tensor FP8 mode).
-    ``v`` is BF16 for ``pv_mode="bf16"`` or E4M3 codes for ``pv_mode="fp8"`` (unscaled, see
-    :func:`cast_e4m3`). Descales are floats or fp32 tensors broadcastable to (num_seqs, heads).
+    ``v`` is BF16 for ``pv_mode="bf16"``, E4M3 codes for ``pv_mode="fp8"`` (unscaled, see
+    :func:`cast_e4m3`) or an :class:`Mxfp8TokensTensor` for ``pv_mode="mx"`` (MX Q and K only). Descales are floats or fp32 tensors broadcastable to (num_seqs, heads).
     ``timing``: optional (start, stop) ``torch.cuda.Event`` pair with timing enabled, each
     recorded once before (so the handles exist); the kernel's dispatch stamps them, and
     ``start.elapsed_time(stop)`` is then the kernel's own duration.
@@ -366,6 +424,11 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
         raise ValueError("q and k must both be Mxfp8Tensor (MX mode) or both raw E4M3 (per-tensor mode)")
     qp = q.payload if mx_q else _as_codes(q)
     kp = k.payload if mx_k else _as_codes(k)
+    vt = v
+    if pv_mode == "mx":
+        if not isinstance(v, Mxfp8TokensTensor):
+            raise ValueError("pv_mode='mx' needs v as an Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
+        v = v.payload
     for t, name in ((qp, "q"), (kp, "k"), (v, "v")):
         _check_rows(t, name)
     if pv_mode == "bf16" and v.dtype != torch.bfloat16:
@@ -380,4 +443,4 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
     plan = AttnPlan(meta_q, meta_k, h, pv_mode=pv_mode, mx=mx_q, softmax_scale=softmax_scale,
                     q_descale=q_descale, k_descale=k_descale, v_descale=v_descale, tile_order=tile_order,
                     out=out, lse=lse)
-    return plan(q if mx_q else qp, k if mx_k else kp, v, timing=timing)
+    return plan(q if mx_q else qp, k if mx_k else kp, vt if pv_mode == "mx" else v, timing=timing)

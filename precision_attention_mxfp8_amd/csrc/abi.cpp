@@ -50,6 +50,31 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
   return launch_status(lpfa::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize");
 }
 
+int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                                 int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
+                                 int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
+                                 uint8_t* scales, void* stream) {
+  if (int rc = lpfa::check_quantize(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads,
+                                    head_dim, cu_seqlens, cu_scale, num_seqs, total_scale_rows,
+                                    scaling_mode, payload, scales))
+    return rc;
+  lpfa::QuantParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.scaling_mode = scaling_mode;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.num_heads = num_heads;
+  p.num_seqs = num_seqs;
+  p.total_scale_rows = total_scale_rows;
+  p.cu_seqlens = cu_seqlens;
+  p.cu_scale = cu_scale;
+  p.payload = payload;
+  p.scales = scales;
+  return launch_status(lpfa::launch_quantize_tokens(p, static_cast<hipStream_t>(stream)), "token quantize");
+}
+
 int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                      int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
                      void* stream) {
@@ -98,11 +123,12 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   p.vd_sh = a->v_descale_stride_head;
   {
     // one past the last byte of the K and V tensors (the kernel's loads are range-checked)
-    const int64_t vb = a->pv_mode == LPFA_PV_FP8 ? 1 : 2;
+    const int64_t vb = a->pv_mode == LPFA_PV_BF16 ? 2 : 1;
     const int64_t kspan = a->total_k > 0 ? (a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128 : 0;
     const int64_t vspan = a->total_k > 0 ? ((a->total_k - 1) * a->v_stride_tok + (int64_t)(a->num_heads - 1) * a->v_stride_head + 128) * vb : 0;
     p.k_end = a->k + kspan;
     p.k_gmax = a->q_scale != nullptr ? a->k_scale_group_max : nullptr;
+    p.v_scale = a->v_scale;
     p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
   }
   p.total_q = a->total_q;

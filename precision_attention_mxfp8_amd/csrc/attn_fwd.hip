@@ -95,7 +95,10 @@ struct Lay {
   // Dynamic LDS: K and its scales (read with ordinary LDS loads).
   static constexpr int OFF_K = 0;                        // 2 buffers
   static constexpr int OFF_KSC = 2 * K_BYTES;            // 2 buffers
-  static constexpr int GROUP_BYTES = OFF_KSC + 2 * KSC_BYTES;
+  // V's token-block scales (MX V): per buffer 4 rows (32-key quarters) of 128 bytes (d)
+  static constexpr int VSC_BYTES = 4 * 128;
+  static constexpr int OFF_VSC = OFF_KSC + 2 * KSC_BYTES;  // 2 buffers (E4M3 V only)
+  static constexpr int GROUP_BYTES = OFF_VSC + (FP8V ? 2 * VSC_BYTES : 0);
   static constexpr int OFF_RED = Groups<FP8V>::G * GROUP_BYTES;  // guard reduction slots
   // Q fragments (score B operands) of the 4 query waves: per (wave, 16-query tile) two 1 KB
   // halves, lane L's 16-byte pieces at L * 16 (conflict-free 16-byte reads). Reloaded for
@@ -196,7 +199,9 @@ struct PFrag<true> { v8i f8[2]; };
 template <>
 struct PFrag<false> { uint32_t w[4][2][4]; };
 
-template <bool MX, bool FP8V>
+// MX: Q and K carry E8M0 block scales. FP8V: V is E4M3 (two wave groups). VMX: that E4M3 V
+// carries E8M0 scales per 32 tokens (the P V instruction's A-operand scales).
+template <bool MX, bool FP8V, bool VMX>
 struct Attn {
   using L = Lay<FP8V>;
   using PF = PFrag<FP8V>;
@@ -282,15 +287,19 @@ struct Attn {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
   }
 
-  // Key order in LDS for E4M3 V: LDS row 16t + 4g + i of a block holds key 32g + 4t + i
-  // (t = score tile, g = lane group, i = register). A score tile's lane group g then holds keys
-  // of the block's 32-key quarter g only, and so do the P V instruction's 32-slot groups (P is
-  // the B operand as the scores left it, and V's transposed reads follow the LDS rows): with V
-  // in MXFP8 along tokens, slot group g is exactly V's 32-token scale block g. For the rows one
-  // lane fills (LDS rows 32w + 8i + r, r = lane / 8, instruction i of wave w) the key is
-  // perm_base(r) + perm_step(i) with a lane part and a uniform per-instruction part.
-  __device__ __forceinline__ int perm_base(int r) const { return 32 * (r >> 2) + 8 * wave + (r & 3); }
-  __device__ __forceinline__ static int perm_step(int i) { return 64 * (i & 1) + 4 * (i >> 1); }
+  // Key order in LDS for E4M3 V. P (the P V instruction's B operand, as the scores left it)
+  // holds in dword t, byte i of lane group g the key of LDS row 16t + 4g + i, and V's
+  // transposed reads follow the LDS rows the same way. The 16x16x128 FP8 instruction takes
+  // K slots 16g + 4t + i (t < 4) and 64 + 16g + 4(t - 4) + i (t >= 4) from those places, and
+  // applies scale block b to slots 32b .. 32b + 31. LDS row 16t + 4g + i therefore holds key
+  // 64(t/4) + 16g + 4(t%4) + i: slot s then carries key s, and with V in MXFP8 along tokens
+  // scale block b is exactly V's 32-token block b of the key block. For the rows one lane fills
+  // (LDS rows 32w + 8i + r, r = lane / 8, instruction i of wave w) the key is
+  // perm_base(r) + perm_step(i): a lane part and a uniform per-instruction part.
+  __device__ __forceinline__ int perm_base(int r) const {
+    return 16 * (r >> 2) + (r & 3) + 64 * (wave >> 1) + 8 * (wave & 1);
+  }
+  __device__ __forceinline__ static int perm_step(int i) { return 32 * (i & 1) + 4 * (i >> 1); }
 
   // K block b into K buffer buf of wave group tg (the issuing wave's group may differ; tg is a
   // constant at every call).
@@ -315,8 +324,8 @@ struct Attn {
                                                  off + (uint32_t)(8 * i) * (uint32_t)k_st_b, 0, 0, 0);
     }
     if (MX && wave < 2) {
-      // scale words of LDS rows 64w + L (w = 0, 1): key 32((L/4)%4) + 4(4w + L/16) + L%4 with E4M3 V
-      const int krow = FP8V ? 32 * ((lane >> 2) & 3) + 4 * (4 * wave + (lane >> 4)) + (lane & 3) : 64 * wave + lane;
+      // scale words of LDS rows 64w + L (w = 0, 1): key 64w + 16((L/4)%4) + 4(L/16) + L%4 with E4M3 V
+      const int krow = FP8V ? 64 * wave + 16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3) : 64 * wave + lane;
       const auto rs = rsrc(ksc_base + (int64_t)(b * BN) * H * 4, ksc_base + (int64_t)(b * BN + BN) * H * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(area + L::OFF_KSC + buf * L::KSC_BYTES + wave * 256), 4,
                                                (uint32_t)(krow * H * 4), 0, 0, 0);
@@ -337,6 +346,13 @@ struct Attn {
       for (int i = 0; i < N; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
                                                  ((i & 2) ? off1 : off0) + (uint32_t)perm_step(i) * (uint32_t)v_st_b, 0, 0, 0);
+      if (VMX && wave < 2) {  // the block's 4 scale rows (32-key quarters), 2 per wave
+        const uint8_t* sb = p.v_scale + (((int64_t)sck / 32 + 4 * b + 2 * wave) * H + head) * 128;
+        const auto rs = rsrc(sb, sb + (int64_t)H * 128 + 128);
+        LDS uint8_t* sd = LDS_PTR(uint8_t, lds + (obj - grp) * L::GROUP_BYTES + L::OFF_VSC + y * L::VSC_BYTES + wave * 256);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)sd, 4, (uint32_t)((lane >> 5) * H * 128 + (lane & 31) * 4),
+                                                 0, 0, 0);
+      }
     } else {
       const uint8_t* row0 = vbase + (int64_t)(b * BN + N * ROWS * wave) * v_st_b;
       const uint32_t off0 = v_off(0);
@@ -574,16 +590,23 @@ struct Attn {
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     if constexpr (FP8V) {
       // software-pipelined: the transposed reads of d tile dt+1 are issued before the matrix
-      // instructions of tile dt, so their latency overlaps
+      // instructions of tile dt, so their latency overlaps. MX V: lane (n, g) supplies the
+      // scale of V^T row 16 dt + n over the block's 32-key quarter g (the slot group g).
+      LDS const uint8_t* vsc = lds_at<const uint8_t>(lds_base + L::OFF_VSC + y * L::VSC_BYTES + g * 128 + n16);
       v8i nxt = v_frag8(v_lane, 0, jj);
+      int snxt = VMX ? (int)vsc[0] : 127;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const v8i vf = nxt;
-        if (dt < 7) nxt = v_frag8(v_lane, dt + 1, jj);
+        const int sc = snxt;
+        if (dt < 7) {
+          nxt = v_frag8(v_lane, dt + 1, jj);
+          if (VMX) snxt = (int)vsc[16 * (dt + 1)];
+        }
         region_end();
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          o[dt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, pf.f8[nt], o[dt][nt], 0, 0, 0, 127, 0, 127);
+          o[dt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf, pf.f8[nt], o[dt][nt], 0, 0, 0, sc, 0, 127);
       }
     } else {
 #pragma unroll
@@ -644,7 +667,7 @@ struct Attn {
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (kb + 32 * g + 4 * mt + i >= Lk) {  // the permuted key order of dma_k
+          if (kb + 64 * (mt >> 2) + 16 * g + 4 * (mt & 3) + i >= Lk) {  // the key order of dma_k
             s[mt][0][i] = -INFINITY;
             s[mt][1][i] = -INFINITY;
           }
@@ -1152,7 +1175,7 @@ struct Attn {
 // path (256 registers per wave) is register-allocated without it: sharing one allocation costs
 // the FP8 path spills around its loops. Only tiles that fail the precision guard make the call
 // (which also saves the registers the calling convention asks the callee to preserve).
-template <bool MX, bool FP8V>
+template <bool MX, bool FP8V, bool VMX>
 __device__ __attribute__((noinline)) void slow_tile(const AttnParams* pp, uint8_t* smem, LDS uint8_t* va,
                                                     LDS uint8_t* vb, int grp, int seq, int head, int qtile) {
   // arguments arrive in vector registers: the uniform ones go back to scalar registers
@@ -1160,14 +1183,14 @@ __device__ __attribute__((noinline)) void slow_tile(const AttnParams* pp, uint8_
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
   const AttnParams& p = *reinterpret_cast<const AttnParams*>((uintptr_t)(((uint64_t)hi << 32) | lo));
-  Attn<MX, FP8V> a(p, smem, __builtin_amdgcn_readfirstlane(grp), va, vb);
+  Attn<MX, FP8V, VMX> a(p, smem, __builtin_amdgcn_readfirstlane(grp), va, vb);
   a.seq = __builtin_amdgcn_readfirstlane(seq);
   a.head = __builtin_amdgcn_readfirstlane(head);
   a.load_meta();
   a.template run<1>(__builtin_amdgcn_readfirstlane(qtile));
 }
 
-template <bool MX, bool FP8V>
+template <bool MX, bool FP8V, bool VMX>
 __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   int seq, head, qtile;
@@ -1188,7 +1211,7 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
   __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V>::VOBJ_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V>::VOBJ_BYTES];
   const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
-  Attn<MX, FP8V> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
+  Attn<MX, FP8V, VMX> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
   a.seq = seq;
   a.head = head;
   a.load_meta();
@@ -1204,11 +1227,11 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
 #else
     const AttnParams* pp = nullptr;
 #endif
-    slow_tile<MX, FP8V>(pp, smem, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb), grp, seq, head, qtile);
+    slow_tile<MX, FP8V, VMX>(pp, smem, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb), grp, seq, head, qtile);
   }
 }
 
-template <bool MX, bool FP8V>
+template <bool MX, bool FP8V, bool VMX>
 hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // Raising the dynamic LDS limit is a per-kernel, per-device attribute: done once per device.
   static std::atomic<uint64_t> configured{0};
@@ -1219,19 +1242,19 @@ hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEven
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
   if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
   if (start == nullptr && stop == nullptr) {
-    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V>), grid, block, bytes, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V, VMX>), grid, block, bytes, s, p);
     return hipGetLastError();
   }
   // The dispatch itself stamps the events: their interval is the kernel, without launch gaps.
   AttnParams arg = p;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V>), grid, block, args,
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX>), grid, block, args,
                             bytes, s, start, stop, 0);
 }
 
@@ -1249,10 +1272,11 @@ hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream
   unsigned grid = (unsigned)p.num_tiles;
   if (p.tile_order == nullptr) grid = (grid + 7u) & ~7u;  // XCD remap needs a multiple of 8
   const bool fp8v = pv_mode == LPFA_PV_FP8;
-  if (mx && fp8v) return launch_variant<true, true>(p, dim3(grid), s, start, stop);
-  if (mx) return launch_variant<true, false>(p, dim3(grid), s, start, stop);
-  if (fp8v) return launch_variant<false, true>(p, dim3(grid), s, start, stop);
-  return launch_variant<false, false>(p, dim3(grid), s, start, stop);
+  if (pv_mode == LPFA_PV_MX) return launch_variant<true, true, true>(p, dim3(grid), s, start, stop);  // MX Q/K checked
+  if (mx && fp8v) return launch_variant<true, true, false>(p, dim3(grid), s, start, stop);
+  if (mx) return launch_variant<true, false, false>(p, dim3(grid), s, start, stop);
+  if (fp8v) return launch_variant<false, true, false>(p, dim3(grid), s, start, stop);
+  return launch_variant<false, false, false>(p, dim3(grid), s, start, stop);
 }
 
 }  // namespace lpfa

@@ -47,8 +47,9 @@ struct AttnParams {
   const int32_t* tile_order;
   uint16_t* out;
   float* lse;
-  const uint8_t* k_end;
-  const uint8_t* k_gmax;  // optional per-(16-row scale group, head) maximum K scale byte  // one past the last byte of K / V: loads beyond read zeros
+  const uint8_t* k_gmax;   // optional per-(16-row scale group, head) maximum K scale byte
+  const uint8_t* v_scale;  // V's token-block scales (MX V only)
+  const uint8_t* k_end;    // one past the last byte of K / V: loads beyond read zeros
   const uint8_t* v_end;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;  // elements
   int64_t qd_ss, qd_sh, kd_ss, kd_sh, vd_ss, vd_sh;
@@ -61,6 +62,7 @@ struct AttnParams {
 };
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s);  // scales: token orientation
 hipError_t launch_cast(const CastParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

@@ -16,6 +16,8 @@
 //   Optionally the workgroup also writes the largest scale byte of its 16 rows' real rows (one
 //   byte per 16-row group and head, 0 for a group of pad rows only): the attention kernel's
 //   precision guard bounds |k| with it.
+// The token-orientation quantizer (V for the P V product) takes blocks of 32 consecutive
+// tokens of a sequence per (head, column); its mapping is described at the kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -126,6 +128,90 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
   }
 }
 
+// Loads 4 consecutive elements (8 bytes BF16, 16 bytes FP32) as floats.
+template <typename T>
+__device__ __forceinline__ void load4(const void* base, int64_t off, float v[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  }
+}
+
+// Token orientation: a workgroup owns one 32-token block (one row of the token-scale storage)
+// of one head. Thread (token group tg = tid / 32, column group cg = tid % 32) holds tokens
+// 4tg..4tg+3 and columns 4cg..4cg+3 (a wave reads two whole 256-byte BF16 rows per load).
+// Column maxima: over the thread's 4 tokens, across the two token groups of a wave (lanes
+// 32 apart), then across the 4 waves through LDS. Each thread then writes its 4x4 codes as
+// four 4-byte words (a wave writes two whole 128-byte payload rows per store), and threads of
+// token group 0 write the 128 scale bytes. Tokens past the sequence's end within its last
+// block are neither read nor written; rows past its last block get 0x7F.
+template <typename T>
+__global__ __launch_bounds__(256) void mxfp8_quantize_tokens_kernel(QuantParams p) {
+  __shared__ float red[4][128];
+  const int h = (int)(blockIdx.x % (unsigned)p.num_heads);
+  const int64_t brow = blockIdx.x / (unsigned)p.num_heads;  // row of the token-scale storage
+  const int tid = threadIdx.x, cg = tid & 31, tg = tid >> 5, wv = tid >> 6;
+  // owning sequence: the largest i with cu_scale[i] / 32 <= brow
+  int lo = 0, hi = p.num_seqs;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if ((int64_t)p.cu_scale[mid] / 32 <= brow) lo = mid; else hi = mid;
+  }
+  const int64_t blk = brow - (int64_t)p.cu_scale[lo] / 32;
+  const int64_t len = (int64_t)p.cu_seqlens[lo + 1] - p.cu_seqlens[lo];
+  uint32_t* scale_words = reinterpret_cast<uint32_t*>(p.scales + (brow * p.num_heads + h) * 128);
+  if (32 * blk >= len) {  // past the sequence's last block (uniform over the workgroup)
+    if (tg == 0) scale_words[cg] = 0x7F7F7F7Fu;
+    return;
+  }
+  const int64_t t0 = p.cu_seqlens[lo] + 32 * blk;
+  const int nval = (int)min<int64_t>(32, len - 32 * blk);  // real tokens in this block
+  float v[4][4];
+  float amax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = 4 * tg + r;
+    const bool in = tok < nval;
+    // a token past the end reads the block's first token (always real) and is then zeroed
+    load4<T>(p.x, (t0 + (in ? tok : 0)) * p.stride_tok + h * p.stride_head + 4 * cg, v[r]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (!in) v[r][c] = 0.0f;
+      amax[c] = fmaxf(amax[c], fabsf(v[r][c]));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    amax[c] = fmaxf(amax[c], __shfl_xor(amax[c], 32));
+    if ((tid & 63) < 32) red[wv][4 * cg + c] = amax[c];
+  }
+  __syncthreads();
+  int e[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = 4 * cg + c;
+    const float m = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+    e[c] = block_exponent(m, p.scaling_mode);
+  }
+  if (tg == 0)
+    scale_words[cg] = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8) | ((uint32_t)(e[2] + 127) << 16) |
+                      ((uint32_t)(e[3] + 127) << 24);
+  float inv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) inv[c] = __uint_as_float((uint32_t)(127 - e[c]) << 23);  // 2^-e, normal
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = 4 * tg + r;
+    if (tok < nval)
+      *reinterpret_cast<uint32_t*>(p.payload + ((t0 + tok) * p.num_heads + h) * 128 + 4 * cg) =
+          cvt4_e4m3(clamp448(v[r][0] * inv[0]), clamp448(v[r][1] * inv[1]), clamp448(v[r][2] * inv[2]),
+                    clamp448(v[r][3] * inv[3]));
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -151,6 +237,17 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
     hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s) {
+  const int64_t blocks = p.total_scale_rows / 32 * p.num_heads;  // one per (32-token block, head)
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  if (p.x_dtype == LPFA_DTYPE_BF16)
+    hipLaunchKernelGGL(mxfp8_quantize_tokens_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(mxfp8_quantize_tokens_kernel<float>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -107,8 +107,14 @@ int check_attn(const lpfa_attn_args* a) {
     return fail(LPFA_EINVAL, "struct_size is smaller than this library's lpfa_attn_args");
   if (a->head_dim != 128) return fail(LPFA_ENOTSUP, "head_dim must be 128");
   if (a->causal != 0) return fail(LPFA_ENOTSUP, "only noncausal attention is implemented");
-  if (a->pv_mode != LPFA_PV_BF16 && a->pv_mode != LPFA_PV_FP8)
-    return fail(LPFA_EINVAL, "pv_mode must be LPFA_PV_BF16 or LPFA_PV_FP8");
+  if (a->pv_mode != LPFA_PV_BF16 && a->pv_mode != LPFA_PV_FP8 && a->pv_mode != LPFA_PV_MX)
+    return fail(LPFA_EINVAL, "pv_mode must be LPFA_PV_BF16, LPFA_PV_FP8 or LPFA_PV_MX");
+  if ((a->pv_mode == LPFA_PV_MX) != (a->v_scale != nullptr))
+    return fail(LPFA_EINVAL, "v_scale is required in the LPFA_PV_MX mode and must be NULL otherwise");
+  if (a->pv_mode == LPFA_PV_MX && a->q_scale == nullptr)
+    return fail(LPFA_EINVAL, "the LPFA_PV_MX mode needs MX Q and K (q_scale and k_scale)");
+  if (a->v_scale && (reinterpret_cast<uintptr_t>(a->v_scale) & 3u))
+    return fail(LPFA_EINVAL, "v_scale must be 4-byte aligned");
   if (a->num_seqs < 0 || a->num_heads < 1 || a->total_q < 0 || a->total_k < 0 ||
       a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
     return fail(LPFA_EINVAL, "negative size, or num_heads < 1");
@@ -121,7 +127,7 @@ int check_attn(const lpfa_attn_args* a) {
   if (a->q_scale && ((reinterpret_cast<uintptr_t>(a->q_scale) & 3u) || (reinterpret_cast<uintptr_t>(a->k_scale) & 3u)))
     return fail(LPFA_EINVAL, "q_scale / k_scale must be 4-byte aligned");
   if (a->v_descale != nullptr && a->pv_mode == LPFA_PV_BF16)
-    return fail(LPFA_EINVAL, "v_descale is only meaningful with FP8 V (pv_mode LPFA_PV_FP8)");
+    return fail(LPFA_EINVAL, "v_descale is only meaningful with FP8 V (pv_mode LPFA_PV_FP8 or LPFA_PV_MX)");
   if (a->num_seqs > 0 && (a->cu_seqlens_q == nullptr || a->cu_seqlens_k == nullptr))
     return fail(LPFA_EINVAL, "cu_seqlens_q / cu_seqlens_k is NULL");
   if (a->max_seqlen_q > a->total_q) return fail(LPFA_EINVAL, "max_seqlen_q exceeds total_q");

@@ -43,7 +43,11 @@ def oracle_operands(wl: Workload, pv_mode: str, mode: str = "mx", descales: Opti
         res.update(pq=pq, pk=pk)
         res["qhat"] = oracle.e4m3_decode(pq)
         res["khat"] = oracle.e4m3_decode(pk)
-    if pv_mode == "fp8":
+    if pv_mode == "mx":   # V MXFP8 along tokens (the oracle's token orientation)
+        pv, sv, csv = oracle.mx_quantize_varlen_tokens(xv, wl.cu_k)
+        res.update(pv=pv, sv=sv)
+        res["vprime"] = oracle.mx_dequantize_varlen_tokens(pv, sv, wl.cu_k, csv)
+    elif pv_mode == "fp8":
         if mode == "mx":
             pv = oracle.e4m3_cast(xv)
         else:

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 2
+    assert lib.lpfa_abi_version() == 3
 
 
 def test_struct_layout_matches_c():
@@ -90,6 +90,26 @@ def test_quantize_rejects(lib, kw, code):
     assert lib.lpfa_last_error().decode()
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), _lib.LPFA_ENOTSUP),
+    (dict(scaling_mode=7), _lib.LPFA_EINVAL),
+    (dict(x=FAKE + 2), _lib.LPFA_EINVAL),
+    (dict(total_scale_rows=100), _lib.LPFA_EINVAL),
+    (dict(scales=None), _lib.LPFA_EINVAL),
+])
+def test_quantize_tokens_rejects(lib, kw, code):
+    args = dict(x=FAKE, x_dtype=0, stride_tok=256, stride_head=128, total_tokens=2, num_heads=2, head_dim=128,
+                cu_seqlens=FAKE, cu_scale=FAKE, num_seqs=1, total_scale_rows=128, scaling_mode=0,
+                payload=FAKE, scales=FAKE)
+    args.update(kw)
+    rc = lib.mxfp8_quantize_varlen_tokens(*[args[k] for k in ("x", "x_dtype", "stride_tok", "stride_head",
+                                                              "total_tokens", "num_heads", "head_dim", "cu_seqlens",
+                                                              "cu_scale", "num_seqs", "total_scale_rows",
+                                                              "scaling_mode", "payload", "scales")], None)
+    assert rc == code
+    assert lib.lpfa_last_error().decode()
+
+
 def test_cast_rejects(lib):
     assert lib.lp_fp8_cast_e4m3(FAKE, 0, 256, 128, 2, 2, 96, FAKE, None) == _lib.LPFA_ENOTSUP
     assert lib.lp_fp8_cast_e4m3(FAKE, 2, 256, 128, 2, 2, 128, FAKE, None) == _lib.LPFA_EINVAL
@@ -119,7 +139,12 @@ def _args(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=64), _lib.LPFA_ENOTSUP),
     (dict(causal=1), _lib.LPFA_ENOTSUP),
-    (dict(pv_mode=2), _lib.LPFA_EINVAL),
+    (dict(pv_mode=3), _lib.LPFA_EINVAL),
+    (dict(pv_mode=2), _lib.LPFA_EINVAL),            # MX V without its scales
+    (dict(pv_mode=1, v_scale=FAKE), _lib.LPFA_EINVAL),   # V scales outside the MX V mode
+    (dict(pv_mode=2, v_scale=FAKE, q_scale=None, k_scale=None, cu_scale_q=None, cu_scale_k=None),
+     _lib.LPFA_EINVAL),                             # MX V needs MX Q and K
+    (dict(pv_mode=2, v_scale=FAKE + 2), _lib.LPFA_EINVAL),  # misaligned V scales
     (dict(struct_size=8), _lib.LPFA_EINVAL),
     (dict(k_scale=None), _lib.LPFA_EINVAL),         # Q scales without K scales
     (dict(q_scale=None), _lib.LPFA_EINVAL),
