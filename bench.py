@@ -13,6 +13,8 @@ timed region, against the dense FP8 matrix peak (stamping a dispatch makes the r
 20 us of extra work for that step, so stamping all of them would slow the step being measured);
 quantizer_gbps / cast_e4m3_gbps = the quantizer and the V cast replayed from a HIP graph of many
 back-to-back launches (eager launches of these short kernels are bound by the host);
+attention_pv_bf16_tflops / attention_pv_mx_tflops = back-to-back forwards with BF16 V and with V
+MXFP8 along tokens, and quantizer_tokens_gbps that V quantizer, graph-replayed;
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
@@ -202,6 +204,19 @@ def main():
         torch.cuda.synchronize()
         bf_ms = a.elapsed_time(b) / n_b2b
         extra["attention_pv_bf16_tflops"] = round(flops / (bf_ms * 1e-3) / 1e12, 2)
+        # MX-scaled V (V MXFP8 along tokens, one scale per 32 tokens per column), and its quantizer
+        vt = lp.quantize_mxfp8_varlen_tokens(v, mk)
+        plan_mx = lp.AttnPlan(mq, mk, h, pv_mode="mx", tile_order=order, out=out, lse=lse)
+        a.record()
+        for _ in range(n_b2b):
+            plan_mx(qx, kx, vt)
+        b.record()
+        torch.cuda.synchronize()
+        mx_ms = a.elapsed_time(b) / n_b2b
+        extra["attention_pv_mx_tflops"] = round(flops / (mx_ms * 1e-3) / 1e12, 2)
+        tms = graph_ms_per_call(torch, lambda: lp.quantize_mxfp8_varlen_tokens(v, mk, out=vt))
+        tbytes = v.numel() * 2 + v.numel() + (mk.total_scale_rows // 32) * h * 128
+        extra["quantizer_tokens_gbps"] = round(tbytes / (tms * 1e-3) / 1e9, 1)
 
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     traffic = None
