@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 3
+#define LPFA_ABI_VERSION 4
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -226,6 +226,12 @@ typedef struct lpfa_attn_args {
    * mxfp8_quantize_varlen_tokens, uint8 (cu_scale_k[num_seqs] / 32, num_heads, 128)
    * contiguous; needs the MX mode (q_scale and k_scale set). */
   const uint8_t* v_scale;
+
+  /* 1: the BF16 FlashAttention forward (LP-FA4 README, the BF16 flash_attn_func path): q and k
+   * point to BF16 (total, num_heads, 128) tensors (strides in elements, 16-byte multiples as
+   * bytes), scores are BF16 products summed in FP32, and pv_mode must be LPFA_PV_BF16; q_scale
+   * and k_scale must be NULL (q/k descales still apply). 0: E4M3 q and k as above. */
+  int32_t qk_bf16;
 } lpfa_attn_args;
 
 /*
@@ -235,14 +241,15 @@ typedef struct lpfa_attn_args {
  *
  * For sequence r, head h, query i and key j:
  *   s_ij = softmax_scale * qd * kd * sum_b 2^(eq_ib + ek_jb) * sum_{d in b} q_id k_jd
- *   (eq, ek = 0 in per-tensor mode), running row max m and sum l over key blocks
+ *   (eq, ek = 0 in per-tensor mode; q, k the BF16 values with qk_bf16), running row max m and sum l over key blocks
  *   (online softmax), P rounded to V's type (BF16, or E4M3 with no scale), O_i =
  *   vd * (sum_j P_ij V_j) / l_i rounded to BF16, LSE_i = ln sum_j exp(s_ij). In the
  *   LPFA_PV_MX mode V_j = payload_j * 2^(ev) with ev the scale of token j's 32-token
  *   block in each column.
  * Errors: LPFA_EINVAL (NULL pointers, bad strides/alignment, scale presence mismatch,
  * v_descale with BF16 V, bad pv_mode, v_scale missing in (or given outside) the
- * LPFA_PV_MX mode or without q_scale/k_scale, struct_size too small, non-positive scale);
+ * LPFA_PV_MX mode or without q_scale/k_scale, qk_bf16 with block scales or with V not BF16,
+ * struct_size too small, non-positive scale);
  * LPFA_ENOTSUP (head_dim != 128, causal != 0); LPFA_EIO (launch failure).
  */
 int lp_attn_varlen_fwd(const lpfa_attn_args* args, void* stream);

@@ -20,7 +20,7 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
 PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
            "lp_fp8_cast_e4m3", "lp_attn_varlen_fwd")
@@ -58,6 +58,7 @@ class AttnArgs(ctypes.Structure):
         ("start_event", _p), ("stop_event", _p),
         ("k_scale_group_max", _p),
         ("v_scale", _p),
+        ("qk_bf16", _i32),
     ]
 
 

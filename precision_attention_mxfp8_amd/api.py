@@ -264,15 +264,18 @@ class AttnPlan:
     checked and marshalled once; each call then sets the operand pointers and launches.
 
     Same arguments and semantics as :func:`lp_attn_varlen_fwd`. ``mx`` selects block-scaled
-    QK^T (operands are Mxfp8Tensor) or per-tensor FP8 (operands are raw E4M3 codes). Descale
-    tensors are read at each launch, so they may be updated in place between calls.
+    QK^T (operands are Mxfp8Tensor) or per-tensor FP8 (operands are raw E4M3 codes);
+    ``qk_bf16`` the BF16 FlashAttention forward (BF16 q and k, ``mx=False``, ``pv_mode="bf16"``).
+    Descale tensors are read at each launch, so they may be updated in place between calls.
     """
 
     def __init__(self, meta_q: VarlenMeta, meta_k: VarlenMeta, num_heads: int, pv_mode: str = "bf16",
                  mx: bool = True, softmax_scale: Optional[float] = None, q_descale: Descale = None,
                  k_descale: Descale = None, v_descale: Descale = None,
                  tile_order: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 lse: Optional[torch.Tensor] = None):
+                 lse: Optional[torch.Tensor] = None, qk_bf16: bool = False):
+        if qk_bf16 and (mx or pv_mode != "bf16"):
+            raise ValueError("BF16 q/k (qk_bf16) need mx=False and pv_mode='bf16'")
         if pv_mode not in _lib.PV_MODES:
             raise ValueError(f"pv_mode must be one of {sorted(_lib.PV_MODES)}, got {pv_mode!r}")
         if meta_q.num_seqs != meta_k.num_seqs:
@@ -306,6 +309,7 @@ class AttnPlan:
         a = _lib.AttnArgs()
         a.struct_size = ctypes.sizeof(_lib.AttnArgs)
         a.pv_mode = _lib.PV_MODES[pv_mode]
+        a.qk_bf16 = 1 if qk_bf16 else 0
         if mx:
             a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
         a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
@@ -332,6 +336,8 @@ class AttnPlan:
         self.out, self.lse = out, lse
         self._qshape, self._kshape = (tq, h, HEAD_DIM), (tk, h, HEAD_DIM)
         self._vdtype = torch.bfloat16 if pv_mode == "bf16" else torch.uint8
+        self.qk_bf16 = bool(qk_bf16)
+        self._qkdtype = torch.bfloat16 if qk_bf16 else torch.uint8
         self._dev = out.device                    # indexed ("cuda:0"), as operand tensors report it
 
     def _operand(self, t: torch.Tensor, shape, dtype, name: str) -> None:
@@ -364,10 +370,10 @@ class AttnPlan:
                 raise ValueError("scale tensors do not match the metadata")
         else:
             if isinstance(q, Mxfp8Tensor) or isinstance(k, Mxfp8Tensor):
-                raise ValueError("this plan is per-tensor FP8: q and k must be raw E4M3 codes")
+                raise ValueError("this plan takes raw q and k (E4M3 codes, or BF16 with qk_bf16)")
             qp, kp = q, k
-        self._operand(qp, self._qshape, torch.uint8, "q")
-        self._operand(kp, self._kshape, torch.uint8, "k")
+        self._operand(qp, self._qshape, self._qkdtype, "q")
+        self._operand(kp, self._kshape, self._qkdtype, "k")
         if self.pv_mode == "mx":
             if not isinstance(v, Mxfp8TokensTensor):
                 raise ValueError("pv_mode='mx' needs v as an Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
@@ -410,7 +416,8 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
                        timing: Optional[Tuple] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Noncausal head_dim-128 attention forward over packed sequences -> (out BF16 (Tq,H,128), lse FP32 (H,Tq)).
 
-    ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T) or raw E4M3 codes (per-tensor FP8 mode).
+    ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T), raw E4M3 codes (per-tensor FP8 mode), or
+    BF16 tensors (the BF16 FlashAttention forward: BF16 scores, needs ``pv_mode="bf16"``).
     ``v`` is BF16 for ``pv_mode="bf16"``, E4M3 codes for ``pv_mode="fp8"`` (unscaled, see
     :func:`cast_e4m3`) or an :class:`Mxfp8TokensTensor` for ``pv_mode="mx"`` (MX Q and K only). Descales are floats or fp32 tensors broadcastable to (num_seqs, heads).
     ``timing``: optional (start, stop) ``torch.cuda.Event`` pair with timing enabled, each
@@ -422,8 +429,14 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
     mx_q, mx_k = isinstance(q, Mxfp8Tensor), isinstance(k, Mxfp8Tensor)
     if mx_q != mx_k:
         raise ValueError("q and k must both be Mxfp8Tensor (MX mode) or both raw E4M3 (per-tensor mode)")
-    qp = q.payload if mx_q else _as_codes(q)
-    kp = k.payload if mx_k else _as_codes(k)
+    qk_bf16 = not mx_q and q.dtype == torch.bfloat16
+    if qk_bf16 and k.dtype != torch.bfloat16:
+        raise ValueError("BF16 q needs BF16 k")
+    if qk_bf16:
+        qp, kp = q, k
+    else:
+        qp = q.payload if mx_q else _as_codes(q)
+        kp = k.payload if mx_k else _as_codes(k)
     vt = v
     if pv_mode == "mx":
         if not isinstance(v, Mxfp8TokensTensor):
@@ -442,5 +455,5 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
         raise ValueError("q, k and v must have the same number of heads")
     plan = AttnPlan(meta_q, meta_k, h, pv_mode=pv_mode, mx=mx_q, softmax_scale=softmax_scale,
                     q_descale=q_descale, k_descale=k_descale, v_descale=v_descale, tile_order=tile_order,
-                    out=out, lse=lse)
+                    out=out, lse=lse, qk_bf16=qk_bf16)
     return plan(q if mx_q else qp, k if mx_k else kp, vt if pv_mode == "mx" else v, timing=timing)

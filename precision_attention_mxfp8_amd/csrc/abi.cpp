@@ -124,11 +124,13 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   {
     // one past the last byte of the K and V tensors (the kernel's loads are range-checked)
     const int64_t vb = a->pv_mode == LPFA_PV_BF16 ? 2 : 1;
-    const int64_t kspan = a->total_k > 0 ? (a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128 : 0;
+    const int64_t kb = a->qk_bf16 ? 2 : 1;
+    const int64_t kspan = a->total_k > 0 ? ((a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128) * kb : 0;
     const int64_t vspan = a->total_k > 0 ? ((a->total_k - 1) * a->v_stride_tok + (int64_t)(a->num_heads - 1) * a->v_stride_head + 128) * vb : 0;
     p.k_end = a->k + kspan;
     p.k_gmax = a->q_scale != nullptr ? a->k_scale_group_max : nullptr;
     p.v_scale = a->v_scale;
+    p.qk_bf16 = a->qk_bf16;
     p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
   }
   p.total_q = a->total_q;

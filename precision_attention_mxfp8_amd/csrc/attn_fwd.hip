@@ -87,9 +87,9 @@ constexpr float LAZY_SUM = 256.0f;
 template <bool FP8V>
 struct Groups { static constexpr int G = FP8V ? 2 : 1; };
 
-template <bool FP8V>
+template <bool FP8V, bool QB = false>
 struct Lay {
-  static constexpr int K_BYTES = BN * 128;
+  static constexpr int K_BYTES = BN * (QB ? 256 : 128);  // QB: BF16 keys (256-byte rows)
   static constexpr int KSC_BYTES = BN * 4;
   static constexpr int V_BYTES = FP8V ? BN * 128 : BN * 256;
   // Dynamic LDS: K and its scales (read with ordinary LDS loads).
@@ -200,10 +200,12 @@ template <>
 struct PFrag<false> { uint32_t w[4][2][4]; };
 
 // MX: Q and K carry E8M0 block scales. FP8V: V is E4M3 (two wave groups). VMX: that E4M3 V
-// carries E8M0 scales per 32 tokens (the P V instruction's A-operand scales).
-template <bool MX, bool FP8V, bool VMX>
+// carries E8M0 scales per 32 tokens (the P V instruction's A-operand scales). QB: Q and K are
+// BF16 (the BF16 FlashAttention forward: BF16 scores and BF16 P V, one wave group).
+template <bool MX, bool FP8V, bool VMX, bool QB = false>
 struct Attn {
-  using L = Lay<FP8V>;
+  static_assert(!QB || (!MX && !FP8V && !VMX), "BF16 Q/K come with BF16 V only");
+  using L = Lay<FP8V, QB>;
   using PF = PFrag<FP8V>;
   static constexpr int G = Groups<FP8V>::G;
 
@@ -228,6 +230,7 @@ struct Attn {
 
   // ---- per-wave state ----
   int qsc[2];
+  v8bf qb16[2][4];           // QB: Q fragments, query tile nt, head_dim slice 32u .. 32u + 31
   float qbound;              // max |q| bound of the wave's queries
   uint32_t ksw[8];           // first batch of the guard's K scale words, loaded before Q
   const uint8_t* qrow[2];    // this lane's query rows (nullptr past the end)
@@ -306,7 +309,21 @@ struct Attn {
   __device__ __forceinline__ void dma_k(int tg, int b, int buf) {
     uint8_t* area = lds + (tg - grp) * L::GROUP_BYTES;
     LDS uint8_t* dst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 4 * wave * 1024);
-    if constexpr (FP8V) {
+    if constexpr (QB) {
+      // BF16 rows of 256 bytes: instruction i of wave w fills region 8w + i = rows 32w + 4i ..
+      // 32w + 4i + 3; lane L fills row 32w + 4i + L/16, LDS chunk L%16, with the row's chunk
+      // (L%16) ^ (row%16) (the score reads then hit 16 different banks for 16 rows)
+      LDS uint8_t* qdst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 8 * wave * 1024);
+      const int r16 = lane >> 4;
+      const auto r = rsrc(kbase + (int64_t)(b * BN + 32 * wave) * k_st_b, p.k_end);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + r16;  // (32w + row) % 16 == row % 16
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(qdst + i * 1024), 16,
+                                                 (uint32_t)(row * (int)k_st_b) + 16u * ((lane & 15) ^ (row & 15)),
+                                                 0, 0, 0);
+      }
+    } else if constexpr (FP8V) {
       const int r8 = lane >> 3;
       const uint32_t off = (uint32_t)(perm_base(r8) * (int)k_st_b) + 16u * ((lane & 7) ^ r8);
       const auto r = rsrc(kbase + (int64_t)(b * BN) * k_st_b, p.k_end);
@@ -458,6 +475,25 @@ struct Attn {
     else
       qa = lds_at<const v4u_t>(lds_base - grp * L::GROUP_BYTES + L::OFF_Q + (wave * 2 + nt) * 2048 + lane * 16);
     return make_v8i(qa[0], qa[64]);   // + 1024 bytes
+  }
+
+  // BF16 scores of the block in K buffer buf from BF16 K and Q (QB): per key tile, 4 slices of 32
+  // along head_dim; lane (n, g) reads key row 16t + n, slice u's chunk 4u + g (swizzled).
+  __device__ __forceinline__ void scores_qb(int buf, v4f s[8][2]) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v8bf kf = *lds_at<const v8bf>(lds_base + L::OFF_K + buf * L::K_BYTES + (16 * mt + n16) * 256 +
+                                            16 * ((4 * u + g) ^ n16));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb16[nt][u], acc[nt], 0, 0, 0);
+      }
+      s[mt][0] = acc[0];
+      s[mt][1] = acc[1];
+      region_end();
+    }
   }
 
   __device__ __forceinline__ void scores_fp8(int buf, v4f s[8][2]) {
@@ -785,9 +821,16 @@ struct Attn {
     LDS uint8_t* v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     v8i qf[2];
-    if (DO_QK) {
+    if (DO_QK && !QB) {
       qf[0] = q_frag(0);
       qf[1] = q_frag(1);
+    }
+    LDS const v8bf* kq[4];  // QB: this lane's slice-u chunk of key row n16 (row 16t + n16: + t * 4096 bytes)
+    if constexpr (QB) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kq[u] = reinterpret_cast<LDS const v8bf*>(dyn() + opaque(L::OFF_K + kb1 * L::K_BYTES + n16 * 256 +
+                                                                 16 * ((4 * u + g) ^ n16)));
     }
 
     float rs[2] = {0.0f, 0.0f};
@@ -813,7 +856,17 @@ struct Attn {
           pf_cur.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(s[k][nt][2], s[k][nt][3]);
         }
       }
-      if (DO_QK) {  // scores of block j+1, key tile k (overwrites the consumed tile)
+      if (DO_QK && QB) {  // BF16 scores of block j+1, key tile k
+        v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const v8bf kf = kq[u][k * 256];  // + k * 4096 bytes
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb16[nt][u], acc[nt], 0, 0, 0);
+        }
+        s[k][0] = acc[0];
+        s[k][1] = acc[1];
+      } else if (DO_QK) {  // scores of block j+1, key tile k (overwrites the consumed tile)
         const v8i kf = make_v8i(k_a[k * 128], k_b[k * 128]);            // + k * 2048 bytes
         const int ks = MX ? (int)ksc[64 * k] : 127;
 #pragma unroll
@@ -892,7 +945,12 @@ struct Attn {
     int j = 0;
     if constexpr (G == 1) {
       if (ng > 0) {
-        if (FAST) scores_fp8(0, s); else scores_bf16(0, s);
+        if constexpr (QB)
+          scores_qb(0, s);
+        else if (FAST)
+          scores_fp8(0, s);
+        else
+          scores_bf16(0, s);
       }
       __syncthreads();  // K buffer 0 is reused for blk(2)
       // iteration j writes its probabilities to pa (j even) or pb (j odd) and reads the
@@ -1027,7 +1085,7 @@ struct Attn {
   // tile again with MODE 1 (BF16 scores, no guard), which always completes and returns true.
   template <int MODE>
   __device__ __forceinline__ bool run(int qtile) {
-    constexpr bool GUARD = MODE != 1;     // this call evaluates the guard
+    constexpr bool GUARD = MODE != 1 && !QB;  // this call evaluates the guard (BF16 Q/K need none)
     constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
     H = p.num_heads;
     qtile0 = qtile;
@@ -1047,9 +1105,9 @@ struct Attn {
     const float kd = p.k_descale ? p.k_descale[seq * p.kd_ss + head * p.kd_sh] : 1.0f;
     c = (p.scale_log2 * qd) * kd;  // identical arithmetic with or without descales
 
-    kbase = p.k + (int64_t)k_start * p.k_st + (int64_t)head * p.k_sh;
+    kbase = p.k + ((int64_t)k_start * p.k_st + (int64_t)head * p.k_sh) * (QB ? 2 : 1);
     vbase = reinterpret_cast<const uint8_t*>(p.v) + ((int64_t)k_start * p.v_st + (int64_t)head * p.v_sh) * (FP8V ? 1 : 2);
-    k_st_b = p.k_st;
+    k_st_b = p.k_st * (QB ? 2 : 1);
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)sck * H + head) * 4 : nullptr;
     kgm_base = MX && p.k_gmax ? p.k_gmax + (int64_t)(sck / 16) * H + head : nullptr;
@@ -1066,13 +1124,29 @@ struct Attn {
       }
     }
 
-    // ---- Q fragments: FP8 (score B operand); the guarded path reloads them as BF16 ----
+    // ---- Q fragments: BF16 in registers (QB), or FP8 (score B operand) through LDS; the
+    // guarded path reloads FP8 Q as BF16 ----
+    if constexpr (QB) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int qi = q0 + wave * 32 + nt * 16 + n16;
+        const bool in = qi < Lq;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)(q_start + (in ? qi : Lq - 1)) * p.q_st +
+                             (int64_t)head * p.q_sh;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint4 w = ldg16(qp + 32 * u + 8 * g);  // head_dim 32u + 8g .. 32u + 8g + 7
+          if (!in) w = make_uint4(0, 0, 0, 0);
+          qb16[nt][u] = __builtin_bit_cast(v8bf, w);
+        }
+      }
+    }
     // Branch-free: a row past the sequence's end reads its last row (the tile has at least one)
     // and is then zeroed, so that every load goes out at once.
     uint32_t qmax_code = 0, qmax_scale = 0;
     v8i qf[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < 2 && !QB; ++nt) {
       const int qi = q0 + wave * 32 + nt * 16 + n16;
       const bool in = qi < Lq;
       const int qc = in ? qi : Lq - 1;
@@ -1098,7 +1172,7 @@ struct Attn {
       }
       qmax_scale = max(qmax_scale, in ? (uint32_t)qsc[nt] : 0u);
     }
-    if (grp == 0) {  // both groups hold the same queries: group 0 stores the fragments
+    if (grp == 0 && !QB) {  // both groups hold the same queries: group 0 stores the fragments
       LDS v4u_t* qa = lds_at<v4u_t>(lds_base + L::OFF_Q + wave * 2 * 2048 + lane * 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -1128,7 +1202,9 @@ struct Attn {
       if (GUARD) guard_publish(red);
       wait_vm_all();
       __syncthreads();
-      if (MODE == 1) {
+      if constexpr (QB) {
+        main_loop<true>(niter);
+      } else if (MODE == 1) {
         main_loop<false>(niter);
       } else {
         const bool fast = fp8_scores_ok_tile(red);  // uniform: every wave reads the same slots
@@ -1190,7 +1266,7 @@ __device__ __attribute__((noinline)) void slow_tile(const AttnParams* pp, uint8_
   a.template run<1>(__builtin_amdgcn_readfirstlane(qtile));
 }
 
-template <bool MX, bool FP8V, bool VMX>
+template <bool MX, bool FP8V, bool VMX, bool QB>
 __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   int seq, head, qtile;
@@ -1208,10 +1284,10 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
     head = rest % p.num_heads;
     seq = rest / p.num_heads;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V>::VOBJ_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V>::VOBJ_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t va[Lay<FP8V, QB>::VOBJ_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vb[Lay<FP8V, QB>::VOBJ_BYTES];
   const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
-  Attn<MX, FP8V, VMX> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
+  Attn<MX, FP8V, VMX, QB> a(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
   a.seq = seq;
   a.head = head;
   a.load_meta();
@@ -1231,30 +1307,30 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
   }
 }
 
-template <bool MX, bool FP8V, bool VMX>
+template <bool MX, bool FP8V, bool VMX, bool QB = false>
 hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // Raising the dynamic LDS limit is a per-kernel, per-device attribute: done once per device.
   static std::atomic<uint64_t> configured{0};
-  const int bytes = Lay<FP8V>::TOTAL;
+  const int bytes = Lay<FP8V, QB>::TOTAL;
   const dim3 block(256 * Groups<FP8V>::G);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
   if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX, QB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
   if (start == nullptr && stop == nullptr) {
-    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V, VMX>), grid, block, bytes, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<MX, FP8V, VMX, QB>), grid, block, bytes, s, p);
     return hipGetLastError();
   }
   // The dispatch itself stamps the events: their interval is the kernel, without launch gaps.
   AttnParams arg = p;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX>), grid, block, args,
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<MX, FP8V, VMX, QB>), grid, block, args,
                             bytes, s, start, stop, 0);
 }
 
@@ -1272,6 +1348,7 @@ hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream
   unsigned grid = (unsigned)p.num_tiles;
   if (p.tile_order == nullptr) grid = (grid + 7u) & ~7u;  // XCD remap needs a multiple of 8
   const bool fp8v = pv_mode == LPFA_PV_FP8;
+  if (p.qk_bf16) return launch_variant<false, false, false, true>(p, dim3(grid), s, start, stop);  // BF16 V checked
   if (pv_mode == LPFA_PV_MX) return launch_variant<true, true, true>(p, dim3(grid), s, start, stop);  // MX Q/K checked
   if (mx && fp8v) return launch_variant<true, true, false>(p, dim3(grid), s, start, stop);
   if (mx) return launch_variant<true, false, false>(p, dim3(grid), s, start, stop);

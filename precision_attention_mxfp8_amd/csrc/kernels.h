@@ -59,6 +59,7 @@ struct AttnParams {
   int32_t q_tiles;    // 128-query tiles per (sequence, head) in the default order
   int32_t num_tiles;  // work tiles to run
   float scale_log2;   // softmax_scale * log2(e)
+  int32_t qk_bf16;    // Q and K are BF16 (the BF16 FlashAttention forward)
 };
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);

@@ -111,6 +111,11 @@ int check_attn(const lpfa_attn_args* a) {
     return fail(LPFA_EINVAL, "pv_mode must be LPFA_PV_BF16, LPFA_PV_FP8 or LPFA_PV_MX");
   if ((a->pv_mode == LPFA_PV_MX) != (a->v_scale != nullptr))
     return fail(LPFA_EINVAL, "v_scale is required in the LPFA_PV_MX mode and must be NULL otherwise");
+  if (a->qk_bf16 != 0 && a->qk_bf16 != 1) return fail(LPFA_EINVAL, "qk_bf16 must be 0 or 1");
+  if (a->qk_bf16 && (a->q_scale != nullptr || a->k_scale != nullptr))
+    return fail(LPFA_EINVAL, "BF16 Q/K (qk_bf16) take no block scales");
+  if (a->qk_bf16 && a->pv_mode != LPFA_PV_BF16)
+    return fail(LPFA_EINVAL, "BF16 Q/K (qk_bf16) need BF16 V (pv_mode LPFA_PV_BF16)");
   if (a->pv_mode == LPFA_PV_MX && a->q_scale == nullptr)
     return fail(LPFA_EINVAL, "the LPFA_PV_MX mode needs MX Q and K (q_scale and k_scale)");
   if (a->v_scale && (reinterpret_cast<uintptr_t>(a->v_scale) & 3u))
@@ -132,8 +137,9 @@ int check_attn(const lpfa_attn_args* a) {
     return fail(LPFA_EINVAL, "cu_seqlens_q / cu_seqlens_k is NULL");
   if (a->max_seqlen_q > a->total_q) return fail(LPFA_EINVAL, "max_seqlen_q exceeds total_q");
   if (a->max_seqlen_k > a->total_k) return fail(LPFA_EINVAL, "max_seqlen_k exceeds total_k");
-  if (int rc = check_rows("q", a->q, a->q_stride_tok, a->q_stride_head, a->total_q, a->num_heads, 1)) return rc;
-  if (int rc = check_rows("k", a->k, a->k_stride_tok, a->k_stride_head, a->total_k, a->num_heads, 1)) return rc;
+  const int qksize = a->qk_bf16 ? 2 : 1;
+  if (int rc = check_rows("q", a->q, a->q_stride_tok, a->q_stride_head, a->total_q, a->num_heads, qksize)) return rc;
+  if (int rc = check_rows("k", a->k, a->k_stride_tok, a->k_stride_head, a->total_k, a->num_heads, qksize)) return rc;
   int vsize = a->pv_mode == LPFA_PV_BF16 ? 2 : 1;
   if (int rc = check_rows("v", a->v, a->v_stride_tok, a->v_stride_head, a->total_k, a->num_heads, vsize)) return rc;
   if (int rc = check_descale("q_descale", a->q_descale, a->q_descale_stride_seq, a->q_descale_stride_head)) return rc;

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 3
+    assert lib.lpfa_abi_version() == 4
 
 
 def test_struct_layout_matches_c():
@@ -145,6 +145,10 @@ def _args(**kw):
     (dict(pv_mode=2, v_scale=FAKE, q_scale=None, k_scale=None, cu_scale_q=None, cu_scale_k=None),
      _lib.LPFA_EINVAL),                             # MX V needs MX Q and K
     (dict(pv_mode=2, v_scale=FAKE + 2), _lib.LPFA_EINVAL),  # misaligned V scales
+    (dict(qk_bf16=1), _lib.LPFA_EINVAL),            # BF16 Q/K with block scales
+    (dict(qk_bf16=1, q_scale=None, k_scale=None, pv_mode=1), _lib.LPFA_EINVAL),   # BF16 Q/K need BF16 V
+    (dict(qk_bf16=1, q_scale=None, k_scale=None, q_stride_tok=100), _lib.LPFA_EINVAL),  # 200 bytes
+    (dict(qk_bf16=2, q_scale=None, k_scale=None), _lib.LPFA_EINVAL),
     (dict(struct_size=8), _lib.LPFA_EINVAL),
     (dict(k_scale=None), _lib.LPFA_EINVAL),         # Q scales without K scales
     (dict(q_scale=None), _lib.LPFA_EINVAL),
