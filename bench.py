@@ -15,6 +15,8 @@ quantizer_gbps / cast_e4m3_gbps = the quantizer and the V cast replayed from a H
 back-to-back launches (eager launches of these short kernels are bound by the host);
 attention_pv_bf16_tflops / attention_pv_mx_tflops = back-to-back forwards with BF16 V and with V
 MXFP8 along tokens, and quantizer_tokens_gbps that V quantizer, graph-replayed;
+attention_bf16_fa_tflops = the BF16 FlashAttention forward (BF16 Q, K, V) on the same shapes,
+back-to-back, and mxfp8_speedup_vs_bf16_fa = its time over the MXFP8 forward's back-to-back time;
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
@@ -217,6 +219,18 @@ def main():
         tms = graph_ms_per_call(torch, lambda: lp.quantize_mxfp8_varlen_tokens(v, mk, out=vt))
         tbytes = v.numel() * 2 + v.numel() + (mk.total_scale_rows // 32) * h * 128
         extra["quantizer_tokens_gbps"] = round(tbytes / (tms * 1e-3) / 1e9, 1)
+        # the BF16 FlashAttention forward on the same shapes (BF16 Q, K, V): the baseline that the
+        # MXFP8 forward's speedup is taken against (both back-to-back, inputs resident)
+        plan_b = lp.AttnPlan(mq, mk, h, pv_mode="bf16", mx=False, qk_bf16=True, tile_order=order, out=out, lse=lse)
+        a.record()
+        for _ in range(n_b2b):
+            plan_b(q, k, v)
+        b.record()
+        torch.cuda.synchronize()
+        bfa_ms = a.elapsed_time(b) / n_b2b
+        extra["attention_bf16_fa_tflops"] = round(flops / (bfa_ms * 1e-3) / 1e12, 2)
+        extra["attention_bf16_fa_pct_bf16_peak"] = round(100 * flops / (bfa_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)
+        extra["mxfp8_speedup_vs_bf16_fa"] = round(bfa_ms / b2b_ms, 3)
 
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     traffic = None
