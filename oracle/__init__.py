@@ -20,6 +20,8 @@ Sources (the pages this project follows):
 * vLLM PR "FA4: no FP8 descale for a unit per-tensor scale": per-tensor q/k/v
   descales; a missing descale reads as 1.0, so a unit descale is bit-identical
   to none, and a descale of 2 changes the output.
+* TensorRT-LLM PR "TE FP8 attention backend for VisualGen": Q/K/V and O scales
+  written from the current tensors before every call (per-tensor current scaling).
 
 Readings taken where the pages are silent are stated in each function.
 
@@ -33,10 +35,11 @@ from .mx import (padded_len, scale_offsets, mx_block_exponent, mx_quantize_varle
                  mx_dequantize_varlen, mx_quantize_varlen_tokens, mx_dequantize_varlen_tokens,
                  e4m3_cast, pertensor_quantize)
 from .attention import attention_varlen, AttentionResult
+from .current import current_scale, current_quantize
 
 __all__ = [
     "E4M3_MAX", "E4M3_VALUES", "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round",
     "bf16_encode", "padded_len", "scale_offsets", "mx_block_exponent", "mx_quantize_varlen",
     "mx_dequantize_varlen", "mx_quantize_varlen_tokens", "mx_dequantize_varlen_tokens", "e4m3_cast", "pertensor_quantize", "attention_varlen",
-    "AttentionResult",
+    "AttentionResult", "current_scale", "current_quantize",
 ]
