@@ -143,6 +143,23 @@ int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t str
                      void* stream);
 
 /*
+ * lp_fp8_cast_current - per-tensor current scaling to E4M3.
+ * (TensorRT-LLM PR "TE FP8 attention backend for VisualGen": the Q/K/V and O scales are
+ *  written from the current tensors before every call, so small tensors such as an attention
+ *  output spread over many keys keep E4M3's normal range.)
+ *
+ *   amax[0] = max |x| over the whole tensor; s = amax / 448 in float32 (s = 1 if amax = 0);
+ *   descale[0] = s; y[t, h, d] = E4M3(x / s) with the quotient rounded to float32, nearest
+ *   even, saturating at 448. x: BF16 or FP32 as in lp_fp8_cast_e4m3; y: uint8 (total_tokens,
+ *   num_heads, 128) contiguous; amax, descale: device float32 (4-byte aligned), written on the
+ *   stream (descale is the per-tensor q/k/v descale of lp_attn_varlen_fwd, strides 0).
+ * Errors: as lp_fp8_cast_e4m3, and LPFA_EINVAL for a NULL or misaligned amax / descale.
+ */
+int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* amax, uint8_t* y,
+                        float* descale, void* stream);
+
+/*
  * Arguments of lp_attn_varlen_fwd. Zero-initialise, then set struct_size =
  * sizeof(lpfa_attn_args); fields added by later ABI versions go at the end.
  */

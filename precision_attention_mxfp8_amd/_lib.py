@@ -23,7 +23,7 @@ PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
 ABI_VERSION = 4
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
-           "lp_fp8_cast_e4m3", "lp_attn_varlen_fwd")
+           "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_attn_varlen_fwd")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -98,6 +98,8 @@ def load() -> ctypes.CDLL:
                                                      _i32, _i64, ctypes.c_int, _p, _p, _p]
         lib.lp_fp8_cast_e4m3.restype = ctypes.c_int
         lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p]
+        lib.lp_fp8_cast_current.restype = ctypes.c_int
+        lib.lp_fp8_cast_current.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p]
         lib.lp_attn_varlen_fwd.restype = ctypes.c_int
         lib.lp_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnArgs), _p]
         _lib = lib

@@ -216,6 +216,26 @@ def cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tens
     return out
 
 
+def cast_e4m3_current(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-tensor current scaling to E4M3: (codes, descale) with descale = amax(|x|) / 448 (float32,
+    1 for an all-zero tensor) as a (1, 1) float32 GPU tensor and codes = E4M3(x / descale). The
+    descale plugs into :func:`lp_attn_varlen_fwd` as a per-tensor q/k/v descale, or dequantizes an
+    FP8 output."""
+    dt = _fp_input(x)
+    t, h, _ = x.shape
+    if out is None:
+        out = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
+    else:
+        _check_out(out, (t, h, HEAD_DIM), torch.uint8, x.device, "out")
+    amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+    descale = torch.empty((1, 1), dtype=torch.float32, device=x.device)
+    rc = _lib.load().lp_fp8_cast_current(x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM,
+                                         amax.data_ptr(), out.data_ptr(), descale.data_ptr(), _stream())
+    if rc:
+        _lib.check("lp_fp8_cast_current", rc)
+    return out, descale
+
+
 def _as_codes(t: torch.Tensor) -> torch.Tensor:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8)

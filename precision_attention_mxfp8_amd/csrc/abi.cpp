@@ -91,6 +91,32 @@ int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t str
   return launch_status(lpfa::launch_cast(p, static_cast<hipStream_t>(stream)), "e4m3 cast");
 }
 
+int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* amax, uint8_t* y,
+                        float* descale, void* stream) {
+  if (int rc = lpfa::check_cast(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads, head_dim, y))
+    return rc;
+  if (amax == nullptr || descale == nullptr) {
+    lpfa::set_error("amax / descale is NULL");
+    return LPFA_EINVAL;
+  }
+  if ((reinterpret_cast<uintptr_t>(amax) & 3u) || (reinterpret_cast<uintptr_t>(descale) & 3u)) {
+    lpfa::set_error("amax / descale is not 4-byte aligned");
+    return LPFA_EINVAL;
+  }
+  lpfa::CastParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.total_tokens = total_tokens;
+  p.num_heads = num_heads;
+  p.y = y;
+  p.amax = amax;
+  p.descale = descale;
+  return launch_status(lpfa::launch_cast_current(p, static_cast<hipStream_t>(stream)), "current-scaled cast");
+}
+
 int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   if (int rc = lpfa::check_attn(a)) return rc;
   lpfa::AttnParams p{};

@@ -29,6 +29,8 @@ struct CastParams {
   int64_t total_tokens;
   int32_t num_heads;
   uint8_t* y;
+  float* amax;     // current scaling: the tensor's largest magnitude (written, then read)
+  float* descale;  // current scaling: s = amax / 448 (1 for an all-zero tensor)
 };
 
 struct AttnParams {
@@ -65,6 +67,7 @@ struct AttnParams {
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s);  // scales: token orientation
 hipError_t launch_cast(const CastParams& p, hipStream_t s);
+hipError_t launch_cast_current(const CastParams& p, hipStream_t s);  // amax, then E4M3(x / s)
 hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 

@@ -227,7 +227,70 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
 }
 
+// ---- per-tensor current scaling (TensorRT-LLM TE-backend PR: Q/K/V and O scales written from
+// the current tensors before every call): amax over the whole tensor, then E4M3(x / s) with
+// s = amax / 448 in float32 (1 for an all-zero tensor). Same lane map as the cast.
+__global__ void amax_init_kernel(float* amax) { *amax = 0.0f; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void amax_kernel(CastParams p) {
+  __shared__ float red[4];
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t head_row = gid >> 4;
+  float m = 0.0f;
+  if (head_row < p.total_tokens * p.num_heads) {
+    const int64_t t = head_row / p.num_heads;
+    const int h = (int)(head_row - t * p.num_heads);
+    float v[8];
+    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + (threadIdx.x & 15) * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // non-negative floats order like their bit patterns: an unsigned maximum is the float maximum
+    atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(m));
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void cast_current_kernel(CastParams p) {
+  const float amax = *p.amax;
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division (round to nearest)
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid == 0) *p.descale = s;
+  const int64_t head_row = gid >> 4;
+  if (head_row >= p.total_tokens * p.num_heads) return;
+  const int64_t t = head_row / p.num_heads;
+  const int h = (int)(head_row - t * p.num_heads);
+  const int sub = threadIdx.x & 15;
+  float v[8];
+  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = clamp448(v[i] / s);  // the quotient rounded to float32 first
+  const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
+  *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
+}
+
 }  // namespace
+
+hipError_t launch_cast_current(const CastParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, p.amax);
+  const int64_t threads = p.total_tokens * p.num_heads * 16;
+  const dim3 grid((unsigned)(threads > 0 ? (threads + 255) / 256 : 1));  // one block writes descale
+  if (p.x_dtype == LPFA_DTYPE_BF16) {
+    if (threads > 0) hipLaunchKernelGGL(amax_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(cast_current_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  } else {
+    if (threads > 0) hipLaunchKernelGGL(amax_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(cast_current_kernel<float>, grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
   const int64_t groups = p.total_scale_rows / 16 * p.num_heads;  // scale rows: whole 128-row blocks
