@@ -17,6 +17,7 @@ attention_pv_bf16_tflops / attention_pv_mx_tflops = back-to-back forwards with B
 MXFP8 along tokens, and quantizer_tokens_gbps that V quantizer, graph-replayed;
 attention_bf16_fa_tflops = the BF16 FlashAttention forward (BF16 Q, K, V) on the same shapes,
 back-to-back, and mxfp8_speedup_vs_bf16_fa = its time over the MXFP8 forward's back-to-back time;
+cast_current_gbps = per-tensor current scaling of V (amax, then the scaled cast), graph-replayed;
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
@@ -194,6 +195,10 @@ def main():
         if pv_mode == "fp8":
             cms = graph_ms_per_call(torch, lambda: lp.cast_e4m3(v, out=vx))
             cast_gbps = v.numel() * 3 / (cms * 1e-3) / 1e9
+            # per-tensor current scaling of the same V (amax pass, then the scaled cast): the
+            # algorithmic bytes are those of one cast (3 B per element); the amax pass reads V again
+            cur_ms = graph_ms_per_call(torch, lambda: lp.cast_e4m3_current(v, out=vx))
+            state["cast_current_gbps"] = round(v.numel() * 3 / (cur_ms * 1e-3) / 1e9, 1)
 
     # ---- pv bf16 variant of the same workload, for the record ----
     extra = {}
@@ -276,6 +281,8 @@ def main():
         "cast_e4m3_gbps": None if cast_gbps is None else round(cast_gbps, 1),
         "pct_fp8_peak": round(100 * achieved / FP8_PEAK_TFLOPS, 2),
     }
+    if "cast_current_gbps" in state:
+        extra["cast_current_gbps"] = state["cast_current_gbps"]
     line.update(extra)
     print(json.dumps(line), flush=True)
 

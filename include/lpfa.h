@@ -148,15 +148,18 @@ int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t str
  *  written from the current tensors before every call, so small tensors such as an attention
  *  output spread over many keys keep E4M3's normal range.)
  *
- *   amax[0] = max |x| over the whole tensor; s = amax / 448 in float32 (s = 1 if amax = 0);
+ *   amax = max |x| over the whole tensor; s = amax / 448 in float32 (s = 1 if amax = 0);
  *   descale[0] = s; y[t, h, d] = E4M3(x / s) with the quotient rounded to float32, nearest
  *   even, saturating at 448. x: BF16 or FP32 as in lp_fp8_cast_e4m3; y: uint8 (total_tokens,
- *   num_heads, 128) contiguous; amax, descale: device float32 (4-byte aligned), written on the
- *   stream (descale is the per-tensor q/k/v descale of lp_attn_varlen_fwd, strides 0).
- * Errors: as lp_fp8_cast_e4m3, and LPFA_EINVAL for a NULL or misaligned amax / descale.
+ *   num_heads, 128) contiguous; descale: device float32, 4-byte aligned (the per-tensor q/k/v
+ *   descale of lp_attn_varlen_fwd, strides 0); work: caller-owned device workspace of
+ *   LPFA_CURRENT_WORK_FLOATS floats (partial maxima between the two kernels, no clearing
+ *   needed); on completion work[0] = amax. Calls that share a work buffer on one stream run
+ *   in order; concurrent calls need their own.
+ * Errors: as lp_fp8_cast_e4m3, and LPFA_EINVAL for a NULL or misaligned work / descale.
  */
 int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
-                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* amax, uint8_t* y,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* work, uint8_t* y,
                         float* descale, void* stream);
 
 /*

@@ -227,10 +227,10 @@ def cast_e4m3_current(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> Tu
         out = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
     else:
         _check_out(out, (t, h, HEAD_DIM), torch.uint8, x.device, "out")
-    amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+    work = torch.empty((257,), dtype=torch.float32, device=x.device)   # LPFA_CURRENT_WORK_FLOATS
     descale = torch.empty((1, 1), dtype=torch.float32, device=x.device)
     rc = _lib.load().lp_fp8_cast_current(x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM,
-                                         amax.data_ptr(), out.data_ptr(), descale.data_ptr(), _stream())
+                                         work.data_ptr(), out.data_ptr(), descale.data_ptr(), _stream())
     if rc:
         _lib.check("lp_fp8_cast_current", rc)
     return out, descale

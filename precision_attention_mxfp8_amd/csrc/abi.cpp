@@ -92,16 +92,16 @@ int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t str
 }
 
 int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
-                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* amax, uint8_t* y,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* work, uint8_t* y,
                         float* descale, void* stream) {
   if (int rc = lpfa::check_cast(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads, head_dim, y))
     return rc;
-  if (amax == nullptr || descale == nullptr) {
-    lpfa::set_error("amax / descale is NULL");
+  if (work == nullptr || descale == nullptr) {
+    lpfa::set_error("work / descale is NULL");
     return LPFA_EINVAL;
   }
-  if ((reinterpret_cast<uintptr_t>(amax) & 3u) || (reinterpret_cast<uintptr_t>(descale) & 3u)) {
-    lpfa::set_error("amax / descale is not 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(work) & 3u) || (reinterpret_cast<uintptr_t>(descale) & 3u)) {
+    lpfa::set_error("work / descale is not 4-byte aligned");
     return LPFA_EINVAL;
   }
   lpfa::CastParams p{};
@@ -112,7 +112,7 @@ int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t 
   p.total_tokens = total_tokens;
   p.num_heads = num_heads;
   p.y = y;
-  p.amax = amax;
+  p.amax = work;
   p.descale = descale;
   return launch_status(lpfa::launch_cast_current(p, static_cast<hipStream_t>(stream)), "current-scaled cast");
 }

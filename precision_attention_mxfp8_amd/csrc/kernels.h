@@ -29,7 +29,7 @@ struct CastParams {
   int64_t total_tokens;
   int32_t num_heads;
   uint8_t* y;
-  float* amax;     // current scaling: the tensor's largest magnitude (written, then read)
+  float* amax;     // current scaling: amax[0] = the tensor's largest magnitude; amax[1..256]: partial maxima
   float* descale;  // current scaling: s = amax / 448 (1 for an all-zero tensor)
 };
 

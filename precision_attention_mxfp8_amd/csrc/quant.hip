@@ -229,40 +229,63 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
 
 // ---- per-tensor current scaling (TensorRT-LLM TE-backend PR: Q/K/V and O scales written from
 // the current tensors before every call): amax over the whole tensor, then E4M3(x / s) with
-// s = amax / 448 in float32 (1 for an all-zero tensor). Same lane map as the cast.
-__global__ void amax_init_kernel(float* amax) { *amax = 0.0f; }
+// s = amax / 448 in float32 (1 for an all-zero tensor). Two kernels and no atomics: at most
+// AMAX_BLOCKS workgroups each write the maximum of their share into work[1 + block], and every
+// workgroup of the cast reduces those partial maxima before casting (work[0] receives amax).
+constexpr int AMAX_BLOCKS = 256;
+
+__device__ __forceinline__ int amax_blocks(int64_t chunks) {
+  const int64_t b = (chunks + 255) / 256;
+  return (int)(b < AMAX_BLOCKS ? b : AMAX_BLOCKS);
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void amax_kernel(CastParams p) {
   __shared__ float red[4];
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t head_row = gid >> 4;
+  const int64_t chunks = p.total_tokens * p.num_heads * 16;  // 8-element chunks
+  const int64_t stride = (int64_t)gridDim.x * 256;
   float m = 0.0f;
-  if (head_row < p.total_tokens * p.num_heads) {
-    const int64_t t = head_row / p.num_heads;
-    const int h = (int)(head_row - t * p.num_heads);
-    float v[8];
-    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + (threadIdx.x & 15) * 8, v);
+  // a stride loop with 4 independent 16-byte loads in flight per thread
+  for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < chunks; c0 += 4 * stride) {
+    float v[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < 4; ++u) {
+      int64_t c = c0 + u * stride;
+      c = c < chunks ? c : c0;  // a chunk past the end rereads this thread's first one (no effect on the max)
+      const int64_t head_row = c >> 4;
+      const int64_t t = head_row / p.num_heads;
+      const int h = (int)(head_row - t * p.num_heads);
+      Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + (c & 15) * 8, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    // non-negative floats order like their bit patterns: an unsigned maximum is the float maximum
-    atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(m));
-  }
+  if (threadIdx.x == 0) p.amax[1 + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void cast_current_kernel(CastParams p) {
-  const float amax = *p.amax;
+  __shared__ float red[4];
+  const int64_t chunks = p.total_tokens * p.num_heads * 16;
+  const int nb = chunks > 0 ? amax_blocks(chunks) : 0;
+  float m = (int)threadIdx.x < nb ? p.amax[1 + threadIdx.x] : 0.0f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division (round to nearest)
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid == 0) *p.descale = s;
+  if (gid == 0) {
+    p.amax[0] = amax;
+    *p.descale = s;
+  }
   const int64_t head_row = gid >> 4;
   if (head_row >= p.total_tokens * p.num_heads) return;
   const int64_t t = head_row / p.num_heads;
@@ -279,14 +302,14 @@ __global__ __launch_bounds__(256) void cast_current_kernel(CastParams p) {
 }  // namespace
 
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, p.amax);
-  const int64_t threads = p.total_tokens * p.num_heads * 16;
-  const dim3 grid((unsigned)(threads > 0 ? (threads + 255) / 256 : 1));  // one block writes descale
+  const int64_t chunks = p.total_tokens * p.num_heads * 16;
+  const dim3 grid((unsigned)(chunks > 0 ? (chunks + 255) / 256 : 1));  // one block writes descale
+  const dim3 agrid((unsigned)(grid.x < (unsigned)AMAX_BLOCKS ? grid.x : (unsigned)AMAX_BLOCKS));
   if (p.x_dtype == LPFA_DTYPE_BF16) {
-    if (threads > 0) hipLaunchKernelGGL(amax_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    if (chunks > 0) hipLaunchKernelGGL(amax_kernel<uint16_t>, agrid, dim3(256), 0, s, p);
     hipLaunchKernelGGL(cast_current_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   } else {
-    if (threads > 0) hipLaunchKernelGGL(amax_kernel<float>, grid, dim3(256), 0, s, p);
+    if (chunks > 0) hipLaunchKernelGGL(amax_kernel<float>, agrid, dim3(256), 0, s, p);
     hipLaunchKernelGGL(cast_current_kernel<float>, grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();

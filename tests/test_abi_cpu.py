@@ -113,7 +113,7 @@ def test_quantize_tokens_rejects(lib, kw, code):
 def test_cast_current_rejects(lib):
     f = lib.lp_fp8_cast_current
     assert f(FAKE, 0, 256, 128, 2, 2, 96, FAKE, FAKE, FAKE, None) == _lib.LPFA_ENOTSUP
-    assert f(FAKE, 0, 256, 128, 2, 2, 128, None, FAKE, FAKE, None) == _lib.LPFA_EINVAL    # amax
+    assert f(FAKE, 0, 256, 128, 2, 2, 128, None, FAKE, FAKE, None) == _lib.LPFA_EINVAL    # work
     assert f(FAKE, 0, 256, 128, 2, 2, 128, FAKE, FAKE, None, None) == _lib.LPFA_EINVAL    # descale
     assert f(FAKE, 0, 256, 128, 2, 2, 128, FAKE + 2, FAKE, FAKE, None) == _lib.LPFA_EINVAL
     assert f(FAKE, 3, 256, 128, 2, 2, 128, FAKE, FAKE, FAKE, None) == _lib.LPFA_EINVAL     # dtype

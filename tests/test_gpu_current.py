@@ -37,6 +37,18 @@ def test_fp32_wide_range_and_strided():
     _check_cast(full[:, 1:3, :], x[:, 1:3, :])           # head stride 128, token stride 512
 
 
+@pytest.mark.parametrize("where", ["last", "first", "middle"])
+def test_many_workgroups_ragged_tail(where):
+    """4099 tokens x 5 heads: 327920 eight-element chunks, more than one pass of the 256
+    amax workgroups' 4-deep stride loop (262144 chunks) with a ragged tail; the largest
+    magnitude is planted where the partial maxima must carry it."""
+    rng = np.random.default_rng(602)
+    x = rng.standard_normal((4099, 5, 128)).astype(np.float32)
+    pos = {"last": (4098, 4, 127), "first": (0, 0, 0), "middle": (2049, 2, 77)}[where]
+    x[pos] = -37.5
+    _check_cast(torch.from_numpy(x).cuda(), x)
+
+
 def test_all_zero_and_empty():
     z = torch.zeros((40, 2, 128), dtype=torch.bfloat16, device="cuda")
     codes, s = lp.cast_e4m3_current(z)
