@@ -22,6 +22,8 @@ Sources (the pages this project follows):
   to none, and a descale of 2 changes the output.
 * TensorRT-LLM PR "TE FP8 attention backend for VisualGen": Q/K/V and O scales
   written from the current tensors before every call (per-tensor current scaling).
+* The same LP-FA4 README section for the backward: quantized Q/K/V in both hardware
+  orientations, the forward's output and LSE, dQ in BF16 and dK/dV in BF16 or MXFP8.
 
 Readings taken where the pages are silent are stated in each function.
 
@@ -36,10 +38,11 @@ from .mx import (padded_len, scale_offsets, mx_block_exponent, mx_quantize_varle
                  e4m3_cast, pertensor_quantize)
 from .attention import attention_varlen, AttentionResult
 from .current import current_scale, current_quantize
+from .backward import attention_varlen_bwd, BackwardResult
 
 __all__ = [
     "E4M3_MAX", "E4M3_VALUES", "e4m3_decode", "e4m3_encode", "e8m0_decode", "bf16_round",
     "bf16_encode", "padded_len", "scale_offsets", "mx_block_exponent", "mx_quantize_varlen",
     "mx_dequantize_varlen", "mx_quantize_varlen_tokens", "mx_dequantize_varlen_tokens", "e4m3_cast", "pertensor_quantize", "attention_varlen",
-    "AttentionResult", "current_scale", "current_quantize",
+    "AttentionResult", "current_scale", "current_quantize", "attention_varlen_bwd", "BackwardResult",
 ]
