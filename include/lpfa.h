@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 4
+#define LPFA_ABI_VERSION 5
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -273,6 +273,81 @@ typedef struct lpfa_attn_args {
  * LPFA_ENOTSUP (head_dim != 128, causal != 0); LPFA_EIO (launch failure).
  */
 int lp_attn_varlen_fwd(const lpfa_attn_args* args, void* stream);
+
+/*
+ * lp_attn_varlen_bwd - noncausal varlen attention backward on MXFP8 operands.
+ * (LP-FA4 README, section "MXFP8 forward and backward": the backward takes the quantized Q, K,
+ *  V, each kept in both hardware orientations, the forward's output and LSE and the output
+ *  gradient; it returns dQ in BF16 and dK, dV in BF16 or, with output_mxfp8_dkv, as E4M3
+ *  payloads with one E8M0 scale per 32-element block.)
+ *
+ * With tau = softmax_scale, per sequence r (its queries attend to its keys only) and head:
+ *   P = exp(tau Qd Kd^T - LSE), dP = dO Vd^T, D = rowsum(dO * O), dS = P * (dP - D),
+ *   dV = P^T dO, dK = tau dS^T Qt, dQ = tau dS Kt,
+ * with Qd, Kd, Vd the head_dim-orientation operands (mxfp8_quantize_varlen) and Qt, Kt the
+ * token-orientation ones (mxfp8_quantize_varlen_tokens): each product takes the orientation whose
+ * blocks run along its contraction. The matrix products take P and dS rounded to BF16 (nearest
+ * even) and the operands dequantized exactly into BF16; sums are FP32.
+ *
+ * All tensors are device memory, contiguous, owned by the caller:
+ *   q, k, v          uint8 E4M3 (total_q | total_k, num_heads, 128); 16-byte aligned
+ *   q_scale, ...     uint8 E8M0 (total_scale_rows_q | _k, num_heads, 4), the quantizer's layout
+ *   q_t, k_t         uint8 E4M3 (total, num_heads, 128), token orientation; 16-byte aligned
+ *   q_t_scale, ...   uint8 E8M0 (total_scale_rows / 32, num_heads, 128); 16-byte aligned
+ *   out, dout        BF16 (total_q, num_heads, 128): the forward's output and its gradient
+ *   lse              float32 (num_heads, total_q), natural log, from lp_attn_varlen_fwd
+ *   delta            float32 (num_heads, total_q) workspace, written (D above); 4-byte aligned
+ *   dq               BF16 (total_q, num_heads, 128), written
+ *   dk, dv           BF16 (total_k, num_heads, 128), or with output_mxfp8_dkv = 1 uint8 E4M3
+ *                    payloads of that shape plus dk_scale, dv_scale: uint8 E8M0
+ *                    (total_scale_rows_k, num_heads, 4) laid out as mxfp8_quantize_varlen's
+ *                    output (scaling_mode RCEIL or FLOOR; pad rows 0x7F)
+ * The cu_* arrays are the forward's (int32, num_seqs + 1 entries). A sequence with queries
+ * must have keys (its contents are trusted, as in the forward); one with keys but no queries
+ * gets zero dK and dV. dq, dk and dv are deterministic: no atomics.
+ * Errors: LPFA_EINVAL for a NULL or misaligned pointer, a bad size, enum or struct_size, or
+ * scales given (or missing) against output_mxfp8_dkv; LPFA_ENOTSUP for head_dim != 128 or
+ * causal; LPFA_EIO when a launch fails.
+ */
+typedef struct lpfa_bwd_args {
+  int32_t struct_size;
+  const uint8_t* q;
+  const uint8_t* q_scale;
+  const uint8_t* k;
+  const uint8_t* k_scale;
+  const uint8_t* v;
+  const uint8_t* v_scale;
+  const uint8_t* q_t;
+  const uint8_t* q_t_scale;
+  const uint8_t* k_t;
+  const uint8_t* k_t_scale;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* cu_scale_q;
+  const int32_t* cu_scale_k;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t causal;
+  int64_t total_q;
+  int64_t total_k;
+  int64_t total_scale_rows_q;
+  int64_t total_scale_rows_k;
+  float softmax_scale;
+  int32_t output_mxfp8_dkv;
+  int32_t scaling_mode;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  uint8_t* dk_scale;
+  uint8_t* dv_scale;
+} lpfa_bwd_args;
+
+int lp_attn_varlen_bwd(const lpfa_bwd_args* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,10 +20,10 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
 PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
-           "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_attn_varlen_fwd")
+           "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_attn_varlen_fwd", "lp_attn_varlen_bwd")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -59,6 +59,24 @@ class AttnArgs(ctypes.Structure):
         ("k_scale_group_max", _p),
         ("v_scale", _p),
         ("qk_bf16", _i32),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``lpfa_bwd_args`` (same field order and types)."""
+
+    _fields_ = [
+        ("struct_size", _i32),
+        ("q", _p), ("q_scale", _p), ("k", _p), ("k_scale", _p), ("v", _p), ("v_scale", _p),
+        ("q_t", _p), ("q_t_scale", _p), ("k_t", _p), ("k_t_scale", _p),
+        ("out", _p), ("dout", _p), ("lse", _p),
+        ("cu_seqlens_q", _p), ("cu_seqlens_k", _p), ("cu_scale_q", _p), ("cu_scale_k", _p),
+        ("num_seqs", _i32), ("num_heads", _i32), ("head_dim", _i32), ("causal", _i32),
+        ("total_q", _i64), ("total_k", _i64),
+        ("total_scale_rows_q", _i64), ("total_scale_rows_k", _i64),
+        ("softmax_scale", ctypes.c_float),
+        ("output_mxfp8_dkv", _i32), ("scaling_mode", _i32),
+        ("delta", _p), ("dq", _p), ("dk", _p), ("dv", _p), ("dk_scale", _p), ("dv_scale", _p),
     ]
 
 
@@ -102,6 +120,8 @@ def load() -> ctypes.CDLL:
         lib.lp_fp8_cast_current.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p]
         lib.lp_attn_varlen_fwd.restype = ctypes.c_int
         lib.lp_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnArgs), _p]
+        lib.lp_attn_varlen_bwd.restype = ctypes.c_int
+        lib.lp_attn_varlen_bwd.argtypes = [ctypes.POINTER(BwdArgs), _p]
         _lib = lib
         return lib
 

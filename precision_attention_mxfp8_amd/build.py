@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["quant.hip", "attn_fwd.hip", "abi.cpp", "validate.cpp"]
+SOURCES = ["quant.hip", "attn_fwd.hip", "attn_bwd.hip", "abi.cpp", "validate.cpp"]
 OUTPUT = os.path.join(PKG, "liblpfa.so")
 
 

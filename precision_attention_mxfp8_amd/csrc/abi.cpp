@@ -171,4 +171,43 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
                        "attention");
 }
 
+int lp_attn_varlen_bwd(const lpfa_bwd_args* a, void* stream) {
+  if (int rc = lpfa::check_bwd(a)) return rc;
+  lpfa::BwdParams p{};
+  p.q = a->q;
+  p.q_scale = a->q_scale;
+  p.k = a->k;
+  p.k_scale = a->k_scale;
+  p.v = a->v;
+  p.v_scale = a->v_scale;
+  p.q_t = a->q_t;
+  p.q_t_scale = a->q_t_scale;
+  p.k_t = a->k_t;
+  p.k_t_scale = a->k_t_scale;
+  p.out = static_cast<const uint16_t*>(a->out);
+  p.dout = static_cast<const uint16_t*>(a->dout);
+  p.lse = a->lse;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.cu_scale_q = a->cu_scale_q;
+  p.cu_scale_k = a->cu_scale_k;
+  p.delta = a->delta;
+  p.dq = static_cast<uint16_t*>(a->dq);
+  p.dk = static_cast<uint8_t*>(a->dk);
+  p.dv = static_cast<uint8_t*>(a->dv);
+  p.dk_scale = a->dk_scale;
+  p.dv_scale = a->dv_scale;
+  p.total_q = a->total_q;
+  // with no keys (or no queries) there is nothing to contract: only the other side's zero or
+  // pad outputs are written
+  p.rows_q = a->total_q > 0 ? a->total_scale_rows_q : 0;
+  p.rows_k = a->total_k > 0 ? a->total_scale_rows_k : 0;
+  p.num_seqs = a->num_seqs;
+  p.num_heads = a->num_heads;
+  p.softmax_scale = a->softmax_scale;
+  p.mx_dkv = a->output_mxfp8_dkv;
+  p.scaling_mode = a->scaling_mode;
+  return launch_status(lpfa::launch_attention_bwd(p, static_cast<hipStream_t>(stream)), "attention backward");
+}
+
 }  // extern "C"

@@ -64,11 +64,47 @@ struct AttnParams {
   int32_t qk_bf16;    // Q and K are BF16 (the BF16 FlashAttention forward)
 };
 
+// Attention backward (lp_attn_varlen_bwd); every tensor contiguous, (tokens, heads, 128).
+struct BwdParams {
+  const uint8_t* q;
+  const uint8_t* q_scale;
+  const uint8_t* k;
+  const uint8_t* k_scale;
+  const uint8_t* v;
+  const uint8_t* v_scale;
+  const uint8_t* q_t;        // token orientation
+  const uint8_t* q_t_scale;  // (scale rows / 32, H, 128)
+  const uint8_t* k_t;
+  const uint8_t* k_t_scale;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* cu_scale_q;
+  const int32_t* cu_scale_k;
+  float* delta;  // (H, total_q)
+  uint16_t* dq;
+  uint8_t* dk;   // BF16 bytes or E4M3 payload
+  uint8_t* dv;
+  uint8_t* dk_scale;
+  uint8_t* dv_scale;
+  int64_t total_q;
+  int64_t rows_q;  // total scale rows of Q and K (multiples of 128)
+  int64_t rows_k;
+  int32_t num_seqs;
+  int32_t num_heads;
+  float softmax_scale;
+  int32_t mx_dkv;
+  int32_t scaling_mode;
+};
+
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s);  // scales: token orientation
 hipError_t launch_cast(const CastParams& p, hipStream_t s);
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s);  // amax, then E4M3(x / s)
 hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s);  // D, then dK/dV, then dQ
 
 }  // namespace lpfa

@@ -28,21 +28,6 @@ namespace lpfa {
 
 namespace {
 
-// Block exponent from the bits of amax (a non-negative float).
-//   RCEIL: smallest e with amax <= 448 * 2^e. For amax = 1.m * 2^E (normal), 448 = 1.75 * 2^8,
-//          so e = E - 8 if 1.m <= 1.75 (mantissa field <= 0x600000), else E - 7.
-//   FLOOR: e = floor(log2 amax) - 8 = E - 8.
-// Zero or subnormal amax gives an exponent below -127 under both rules: clamp to -127.
-__device__ __forceinline__ int block_exponent(float amax, int mode) {
-  uint32_t bits = __float_as_uint(amax);
-  int biased = (int)(bits >> 23);
-  uint32_t mant = bits & 0x7FFFFFu;
-  int e = biased - 135;
-  if (mode == LPFA_SCALING_RCEIL && mant > 0x600000u) e += 1;
-  if (biased == 0) e = -127;
-  return e < -127 ? -127 : e;  // the largest finite amax gives e = 120, so no upper clamp is hit
-}
-
 template <typename T>
 struct Loader;
 

@@ -1,6 +1,7 @@
 // Host-side argument checks (see validate.h). The rules restate the contract of include/lpfa.h.
 #include "validate.h"
 
+#include <climits>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -157,6 +158,65 @@ int check_attn(const lpfa_attn_args* a) {
   if (a->total_q * (int64_t)a->num_heads > INT32_MAX || a->total_k * (int64_t)a->num_heads > (int64_t)INT32_MAX * 8)
     return fail(LPFA_ENOTSUP, "tensor too large for one launch");
   clear_error();
+  return LPFA_OK;
+}
+
+int check_bwd(const lpfa_bwd_args* a) {
+  clear_error();
+  if (a == nullptr) return fail(LPFA_EINVAL, "args is NULL");
+  if (a->struct_size < (int32_t)sizeof(lpfa_bwd_args))
+    return fail(LPFA_EINVAL, "struct_size is smaller than this library's lpfa_bwd_args");
+  if (a->head_dim != 128) return fail(LPFA_ENOTSUP, "head_dim must be 128");
+  if (a->causal != 0) return fail(LPFA_ENOTSUP, "only noncausal attention is implemented");
+  if (a->num_seqs < 0 || a->num_heads < 1 || a->total_q < 0 || a->total_k < 0 || a->total_scale_rows_q < 0 ||
+      a->total_scale_rows_k < 0)
+    return fail(LPFA_EINVAL, "negative size, or num_heads < 1");
+  if (a->total_scale_rows_q % 128 != 0 || a->total_scale_rows_k % 128 != 0)
+    return fail(LPFA_EINVAL, "total scale rows must be multiples of 128");
+  if (a->total_scale_rows_q < a->total_q || a->total_scale_rows_k < a->total_k)
+    return fail(LPFA_EINVAL, "total scale rows below the token count");
+  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale > 0.0f))
+    return fail(LPFA_EINVAL, "softmax_scale must be finite and positive");
+  if (a->output_mxfp8_dkv != 0 && a->output_mxfp8_dkv != 1) return fail(LPFA_EINVAL, "output_mxfp8_dkv must be 0 or 1");
+  if (a->scaling_mode != LPFA_SCALING_RCEIL && a->scaling_mode != LPFA_SCALING_FLOOR)
+    return fail(LPFA_EINVAL, "scaling_mode must be RCEIL or FLOOR");
+  if ((a->dk_scale != nullptr || a->dv_scale != nullptr) != (a->output_mxfp8_dkv != 0) ||
+      (a->output_mxfp8_dkv && (a->dk_scale == nullptr || a->dv_scale == nullptr)))
+    return fail(LPFA_EINVAL, "dk_scale and dv_scale are required with output_mxfp8_dkv and rejected without");
+  if (a->num_seqs > 0 && (a->cu_seqlens_q == nullptr || a->cu_seqlens_k == nullptr || a->cu_scale_q == nullptr ||
+                          a->cu_scale_k == nullptr))
+    return fail(LPFA_EINVAL, "cu_seqlens / cu_scale is NULL");
+  if (a->num_seqs == 0 && (a->total_q != 0 || a->total_k != 0))
+    return fail(LPFA_EINVAL, "tokens without sequences");
+  struct Need {
+    const void* ptr;
+    bool used;
+    const char* name;
+    unsigned align;
+  };
+  const bool hq = a->total_q > 0, hk = a->total_k > 0, both = hq && hk;
+  const Need need[] = {
+      {a->q, both, "q", 16u},           {a->q_scale, both, "q_scale", 1u},
+      {a->k, both, "k", 16u},           {a->k_scale, both, "k_scale", 1u},
+      {a->v, both, "v", 16u},           {a->v_scale, both, "v_scale", 1u},
+      {a->q_t, both, "q_t", 16u},       {a->q_t_scale, both, "q_t_scale", 16u},
+      {a->k_t, both, "k_t", 16u},       {a->k_t_scale, both, "k_t_scale", 16u},
+      {a->out, hq, "out", 16u},         {a->dout, hq, "dout", 16u},
+      {a->lse, both, "lse", 4u},        {a->delta, hq, "delta", 4u},
+      {a->dq, hq, "dq", 16u},           {a->dk, hk, "dk", 16u},
+      {a->dv, hk, "dv", 16u},
+  };
+  for (const Need& n : need) {
+    if (!n.used) continue;
+    if (n.ptr == nullptr) return fail(LPFA_EINVAL, std::string(n.name) + " is NULL");
+    if ((reinterpret_cast<uintptr_t>(n.ptr) & (n.align - 1u)) != 0)
+      return fail(LPFA_EINVAL, std::string(n.name) + " is misaligned");
+  }
+  if ((a->total_q + 1) * (int64_t)a->num_heads * 128 * 4 > INT64_MAX / 4 ||
+      a->total_scale_rows_q / 64 > 0x7FFFFFFF || a->total_scale_rows_k / 64 > 0x7FFFFFFF ||
+      (a->total_q * (int64_t)a->num_heads * 16 + 255) / 256 > 0x7FFFFFFF)
+    return fail(LPFA_ENOTSUP, "tensor too large for one launch");
+  if (a->num_heads > 65535) return fail(LPFA_ENOTSUP, "num_heads above the launch grid's limit");
   return LPFA_OK;
 }
 

@@ -21,5 +21,6 @@ int check_quantize(const void* x, int x_dtype, int64_t stride_tok, int64_t strid
 int check_cast(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                int64_t total_tokens, int32_t num_heads, int32_t head_dim, const uint8_t* y);
 int check_attn(const lpfa_attn_args* a);
+int check_bwd(const lpfa_bwd_args* a);
 
 }  // namespace lpfa

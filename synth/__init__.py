@@ -155,3 +155,10 @@ def make_custom(lengths_q: List[int], lengths_k: List[int], heads: int, seed: in
             x[mask] *= np.float32(20.0)
     return Workload("custom", list(lengths_q), list(lengths_k), heads,
                     f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v))
+
+
+def make_output_grad(tokens: int, heads: int, seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """A seeded output gradient dO: N(0, std^2) rounded to BF16 bit patterns, (tokens, heads, 128)
+    (the README's backward example draws it as a standard normal like the output)."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(_normals(rng, tokens, heads, std))

@@ -34,14 +34,15 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 4
+    assert lib.lpfa_abi_version() == 5
 
 
-def test_struct_layout_matches_c():
-    fields = [f[0] for f in _lib.AttnArgs._fields_]
+@pytest.mark.parametrize("cname,pystruct", [("lpfa_attn_args", _lib.AttnArgs), ("lpfa_bwd_args", _lib.BwdArgs)])
+def test_struct_layout_matches_c(cname, pystruct):
+    fields = [f[0] for f in pystruct._fields_]
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "lpfa.h"', "int main(void){",
-           'printf("size %zu\\n", sizeof(lpfa_attn_args));']
-    src += [f'printf("{f} %zu\\n", offsetof(lpfa_attn_args, {f}));' for f in fields]
+           f'printf("size %zu\\n", sizeof({cname}));']
+    src += [f'printf("{f} %zu\\n", offsetof({cname}, {f}));' for f in fields]
     src += ["return 0;}"]
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "layout.c")
@@ -50,9 +51,9 @@ def test_struct_layout_matches_c():
         subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(line.split() for line in out if line.strip())
-    assert int(got["size"]) == ctypes.sizeof(_lib.AttnArgs)
+    assert int(got["size"]) == ctypes.sizeof(pystruct)
     for f in fields:
-        assert int(got[f]) == getattr(_lib.AttnArgs, f).offset, f
+        assert int(got[f]) == getattr(pystruct, f).offset, f
 
 
 FAKE = 0x10000  # an aligned non-NULL address: validation checks it, nothing dereferences it
@@ -184,6 +185,49 @@ def test_attention_rejects(lib, kw, code):
 
 def test_attention_rejects_null_args(lib):
     assert lib.lp_attn_varlen_fwd(None, None) == _lib.LPFA_EINVAL
+    assert lib.lp_attn_varlen_bwd(None, None) == _lib.LPFA_EINVAL
+
+
+def _bwd_args(**kw):
+    a = _lib.BwdArgs()
+    a.struct_size = ctypes.sizeof(_lib.BwdArgs)
+    for f in ("q", "q_scale", "k", "k_scale", "v", "v_scale", "q_t", "q_t_scale", "k_t", "k_t_scale", "out",
+              "dout", "lse", "cu_seqlens_q", "cu_seqlens_k", "cu_scale_q", "cu_scale_k", "delta", "dq", "dk", "dv"):
+        setattr(a, f, FAKE)
+    a.num_seqs, a.num_heads, a.head_dim = 1, 2, 128
+    a.total_q = a.total_k = 100
+    a.total_scale_rows_q = a.total_scale_rows_k = 128
+    a.softmax_scale = 0.088
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), _lib.LPFA_ENOTSUP),
+    (dict(causal=1), _lib.LPFA_ENOTSUP),
+    (dict(struct_size=8), _lib.LPFA_EINVAL),
+    (dict(num_heads=0), _lib.LPFA_EINVAL),
+    (dict(total_scale_rows_k=100), _lib.LPFA_EINVAL),     # not a multiple of 128
+    (dict(total_q=200), _lib.LPFA_EINVAL),                # more tokens than scale rows
+    (dict(softmax_scale=-1.0), _lib.LPFA_EINVAL),
+    (dict(output_mxfp8_dkv=2), _lib.LPFA_EINVAL),
+    (dict(scaling_mode=2), _lib.LPFA_EINVAL),
+    (dict(output_mxfp8_dkv=1), _lib.LPFA_EINVAL),          # MXFP8 dK/dV without scale outputs
+    (dict(output_mxfp8_dkv=1, dk_scale=FAKE), _lib.LPFA_EINVAL),
+    (dict(dk_scale=FAKE, dv_scale=FAKE), _lib.LPFA_EINVAL),  # scale outputs for BF16 dK/dV
+    (dict(q_t=None), _lib.LPFA_EINVAL),
+    (dict(k_t_scale=FAKE + 4), _lib.LPFA_EINVAL),         # token scales are read 16 bytes at a time
+    (dict(dq=FAKE + 2), _lib.LPFA_EINVAL),
+    (dict(lse=FAKE + 2), _lib.LPFA_EINVAL),
+    (dict(delta=None), _lib.LPFA_EINVAL),
+    (dict(cu_scale_k=None), _lib.LPFA_EINVAL),
+    (dict(num_seqs=0), _lib.LPFA_EINVAL),                 # tokens without sequences
+])
+def test_backward_rejects(lib, kw, code):
+    a = _bwd_args(**kw)
+    assert lib.lp_attn_varlen_bwd(ctypes.byref(a), None) == code
+    assert lib.lpfa_last_error().decode()
 
 
 def test_varlen_meta_host_side():
