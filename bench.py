@@ -18,6 +18,8 @@ MXFP8 along tokens, and quantizer_tokens_gbps that V quantizer, graph-replayed;
 attention_bf16_fa_tflops = the BF16 FlashAttention forward (BF16 Q, K, V) on the same shapes,
 back-to-back, and mxfp8_speedup_vs_bf16_fa = its time over the MXFP8 forward's back-to-back time;
 cast_current_gbps = per-tensor current scaling of V (amax, then the scaled cast), graph-replayed;
+attention_bwd_tflops / _us / _pct_bf16_peak = the MXFP8 backward with MXFP8 dK/dV output,
+back-to-back (2.5 x the forward's FLOPs; its matrix products run in BF16);
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense] [--pv-mode fp8]
@@ -236,6 +238,28 @@ def main():
         extra["attention_bf16_fa_tflops"] = round(flops / (bfa_ms * 1e-3) / 1e12, 2)
         extra["attention_bf16_fa_pct_bf16_peak"] = round(100 * flops / (bfa_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)
         extra["mxfp8_speedup_vs_bf16_fa"] = round(bfa_ms / b2b_ms, 3)
+        # the MXFP8 backward with fused MXFP8 dK/dV output (the README times the backward on that
+        # path): D, dK/dV and dQ kernels back-to-back, on the MX-V forward's own output and LSE;
+        # FLOPs = 2.5 x the forward's (five matrix products of the forward's size each)
+        from synth import make_output_grad
+        qt_b = lp.quantize_mxfp8_varlen_tokens(q, mq)
+        kt_b = lp.quantize_mxfp8_varlen_tokens(k, mk)
+        vd_b = lp.quantize_mxfp8_varlen(v, mk)
+        plan_mx(qx, kx, vt)
+        dout = up(make_output_grad(mq.total_tokens, h, seed=1))
+        bplan = lp.BwdPlan(qx, kx, vd_b, qt_b, kt_b, out, dout, lse, output_mxfp8_dkv=True)
+        bplan()
+        torch.cuda.synchronize()
+        n_bwd = max(10, n_b2b // 4)
+        a.record()
+        for _ in range(n_bwd):
+            bplan()
+        b.record()
+        torch.cuda.synchronize()
+        bwd_ms = a.elapsed_time(b) / n_bwd
+        extra["attention_bwd_us"] = round(bwd_ms * 1e3, 2)
+        extra["attention_bwd_tflops"] = round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 2)
+        extra["attention_bwd_pct_bf16_peak"] = round(100 * 2.5 * flops / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)
 
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     traffic = None

@@ -296,7 +296,10 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* args, void* stream);
  *   q_t_scale, ...   uint8 E8M0 (total_scale_rows / 32, num_heads, 128); 16-byte aligned
  *   out, dout        BF16 (total_q, num_heads, 128): the forward's output and its gradient
  *   lse              float32 (num_heads, total_q), natural log, from lp_attn_varlen_fwd
- *   delta            float32 (num_heads, total_q) workspace, written (D above); 4-byte aligned
+ *   work             device workspace of LPFA_BWD_WORK_BYTES(total_q, total_k, num_heads)
+ *                    bytes, 256-byte aligned, overwritten: D above (float32 (num_heads,
+ *                    total_q)), then BF16 copies of Qd, Qt, Kd, Vd, Kt dequantized once so the
+ *                    main kernels stream plain BF16 tiles
  *   dq               BF16 (total_q, num_heads, 128), written
  *   dk, dv           BF16 (total_k, num_heads, 128), or with output_mxfp8_dkv = 1 uint8 E4M3
  *                    payloads of that shape plus dk_scale, dv_scale: uint8 E8M0
@@ -339,13 +342,18 @@ typedef struct lpfa_bwd_args {
   float softmax_scale;
   int32_t output_mxfp8_dkv;
   int32_t scaling_mode;
-  float* delta;
+  void* work;
   void* dq;
   void* dk;
   void* dv;
   uint8_t* dk_scale;
   uint8_t* dv_scale;
 } lpfa_bwd_args;
+
+/* Workspace bytes of lp_attn_varlen_bwd: D rounded up to 256 bytes, then five BF16 copies. */
+#define LPFA_BWD_WORK_BYTES(total_q, total_k, num_heads)                                   \
+  ((((int64_t)(num_heads) * (int64_t)(total_q) * 4 + 255) / 256) * 256 +                  \
+   (int64_t)(num_heads) * 256 * (2 * (int64_t)(total_q) + 3 * (int64_t)(total_k)))
 
 int lp_attn_varlen_bwd(const lpfa_bwd_args* args, void* stream);
 

@@ -4,15 +4,15 @@ Public API (marshalling only; the work runs in liblpfa.so):
   VarlenMeta.from_lengths, quantize_mxfp8_varlen, quantize_mxfp8_varlen_tokens, cast_e4m3,
   cast_e4m3_current (per-tensor current scaling),
   lp_attn_varlen_fwd, AttnPlan (a prepared lp_attn_varlen_fwd for repeated calls),
-  lp_attn_varlen_bwd (gradients on MXFP8 operands; dK/dV in BF16 or MXFP8),
+  lp_attn_varlen_bwd (gradients on MXFP8 operands; dK/dV in BF16 or MXFP8), BwdPlan (prepared),
   longest_first_tile_order.
 """
-from .api import (AttnPlan, Mxfp8Tensor, Mxfp8TokensTensor, VarlenMeta, cast_e4m3, cast_e4m3_current,
+from .api import (AttnPlan, BwdPlan, Mxfp8Tensor, Mxfp8TokensTensor, VarlenMeta, cast_e4m3, cast_e4m3_current,
                   longest_first_tile_order,
                   lp_attn_varlen_bwd, lp_attn_varlen_fwd, quantize_mxfp8_varlen, quantize_mxfp8_varlen_tokens)
 from ._lib import LpfaError, load as load_library
 
-__all__ = ["AttnPlan", "Mxfp8Tensor", "Mxfp8TokensTensor", "VarlenMeta", "cast_e4m3", "cast_e4m3_current",
+__all__ = ["AttnPlan", "BwdPlan", "Mxfp8Tensor", "Mxfp8TokensTensor", "VarlenMeta", "cast_e4m3", "cast_e4m3_current",
            "longest_first_tile_order",
            "lp_attn_varlen_bwd", "lp_attn_varlen_fwd", "quantize_mxfp8_varlen", "quantize_mxfp8_varlen_tokens", "LpfaError",
            "load_library"]

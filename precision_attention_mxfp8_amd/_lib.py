@@ -76,8 +76,13 @@ class BwdArgs(ctypes.Structure):
         ("total_scale_rows_q", _i64), ("total_scale_rows_k", _i64),
         ("softmax_scale", ctypes.c_float),
         ("output_mxfp8_dkv", _i32), ("scaling_mode", _i32),
-        ("delta", _p), ("dq", _p), ("dk", _p), ("dv", _p), ("dk_scale", _p), ("dv_scale", _p),
+        ("work", _p), ("dq", _p), ("dk", _p), ("dv", _p), ("dk_scale", _p), ("dv_scale", _p),
     ]
+
+
+def bwd_work_bytes(total_q: int, total_k: int, num_heads: int) -> int:
+    """LPFA_BWD_WORK_BYTES: D (float32, rounded up to 256 bytes) + five BF16 (tokens, H, 128) copies."""
+    return (num_heads * total_q * 4 + 255) // 256 * 256 + num_heads * 256 * (2 * total_q + 3 * total_k)
 
 
 _lib = None

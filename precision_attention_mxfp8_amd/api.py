@@ -479,6 +479,86 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
     return plan(q if mx_q else qp, k if mx_k else kp, vt if pv_mode == "mx" else v, timing=timing)
 
 
+class BwdPlan:
+    """A prepared :func:`lp_attn_varlen_bwd`: operands checked, outputs allocated and the C
+    arguments marshalled once; each call launches the backward on the current stream and returns
+    the same output objects (overwritten)."""
+
+    def __init__(self, q: Mxfp8Tensor, k: Mxfp8Tensor, v: Mxfp8Tensor,
+                 q_t: Mxfp8TokensTensor, k_t: Mxfp8TokensTensor,
+                 out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                 softmax_scale: Optional[float] = None, output_mxfp8_dkv: bool = False,
+                 scaling_mode: str = "rceil"):
+        if scaling_mode not in _lib.SCALING:
+            raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
+        if not all(isinstance(t, Mxfp8Tensor) for t in (q, k, v)):
+            raise ValueError("q, k and v must be Mxfp8Tensor (quantize_mxfp8_varlen)")
+        if not all(isinstance(t, Mxfp8TokensTensor) for t in (q_t, k_t)):
+            raise ValueError("q_t and k_t must be Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
+        meta_q, meta_k = q.meta, k.meta
+        if v.meta.lengths != meta_k.lengths or q_t.meta.lengths != meta_q.lengths or k_t.meta.lengths != meta_k.lengths:
+            raise ValueError("operands disagree on sequence lengths")
+        if meta_q.num_seqs != meta_k.num_seqs:
+            raise ValueError("query and key metadata must have the same number of sequences")
+        for a_, b_ in zip(meta_q.lengths, meta_k.lengths):
+            if a_ > 0 and b_ == 0:
+                raise ValueError("a sequence with queries needs keys")
+        for t, name in ((q.payload, "q"), (k.payload, "k"), (v.payload, "v"), (q_t.payload, "q_t"),
+                        (k_t.payload, "k_t"), (out, "out"), (dout, "dout")):
+            _check_rows(t, name)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        tq, h = q.payload.shape[0], q.payload.shape[1]
+        tk = k.payload.shape[0]
+        dev = q.payload.device
+        for t, name, shape, dtype in ((out, "out", (tq, h, HEAD_DIM), torch.bfloat16),
+                                      (dout, "dout", (tq, h, HEAD_DIM), torch.bfloat16),
+                                      (lse, "lse", (h, tq), torch.float32)):
+            _check_out(t, shape, dtype, dev, name)
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        self._keep = (q, k, v, q_t, k_t, out, dout, lse)
+        self.work = torch.empty((_lib.bwd_work_bytes(tq, tk, h),), dtype=torch.uint8, device=dev)
+        self.dq = torch.empty((tq, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.mx = bool(output_mxfp8_dkv)
+        if self.mx:
+            dk = torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev)
+            dv = torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev)
+            dks = torch.empty((meta_k.total_scale_rows, h, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
+            dvs = torch.empty((meta_k.total_scale_rows, h, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
+            self.dk, self.dv = Mxfp8Tensor(dk, dks, meta_k), Mxfp8Tensor(dv, dvs, meta_k)
+        else:
+            dk = torch.empty((tk, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+            dv = torch.empty((tk, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+            dks = dvs = None
+            self.dk, self.dv = dk, dv
+        a = _lib.BwdArgs()
+        a.struct_size = ctypes.sizeof(_lib.BwdArgs)
+        a.q, a.q_scale = _ptr(q.payload), _ptr(q.scales)
+        a.k, a.k_scale = _ptr(k.payload), _ptr(k.scales)
+        a.v, a.v_scale = _ptr(v.payload), _ptr(v.scales)
+        a.q_t, a.q_t_scale = _ptr(q_t.payload), _ptr(q_t.scales)
+        a.k_t, a.k_t_scale = _ptr(k_t.payload), _ptr(k_t.scales)
+        a.out, a.dout, a.lse = _ptr(out), _ptr(dout), _ptr(lse)
+        a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
+        a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
+        a.num_seqs, a.num_heads, a.head_dim, a.causal = meta_q.num_seqs, h, HEAD_DIM, 0
+        a.total_q, a.total_k = tq, tk
+        a.total_scale_rows_q, a.total_scale_rows_k = meta_q.total_scale_rows, meta_k.total_scale_rows
+        a.softmax_scale = float(softmax_scale)
+        a.output_mxfp8_dkv = 1 if self.mx else 0
+        a.scaling_mode = _lib.SCALING[scaling_mode]
+        a.work, a.dq, a.dk, a.dv = _ptr(self.work), _ptr(self.dq), _ptr(dk), _ptr(dv)
+        a.dk_scale, a.dv_scale = _ptr(dks), _ptr(dvs)
+        self._args = a
+        self._ref = ctypes.byref(a)
+        self._lib = _lib.load()
+
+    def __call__(self):
+        _lib.check("lp_attn_varlen_bwd", self._lib.lp_attn_varlen_bwd(self._ref, _stream()))
+        return self.dq, self.dk, self.dv
+
+
 def lp_attn_varlen_bwd(q: Mxfp8Tensor, k: Mxfp8Tensor, v: Mxfp8Tensor,
                        q_t: Mxfp8TokensTensor, k_t: Mxfp8TokensTensor,
                        out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
@@ -494,65 +574,4 @@ def lp_attn_varlen_bwd(q: Mxfp8Tensor, k: Mxfp8Tensor, v: Mxfp8Tensor,
     :class:`Mxfp8Tensor` (E4M3 payload and E8M0 scales per 32-element block, K's metadata,
     ``scaling_mode`` RCEIL or FLOOR). dq is BF16 either way.
     """
-    if scaling_mode not in _lib.SCALING:
-        raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
-    if not all(isinstance(t, Mxfp8Tensor) for t in (q, k, v)):
-        raise ValueError("q, k and v must be Mxfp8Tensor (quantize_mxfp8_varlen)")
-    if not all(isinstance(t, Mxfp8TokensTensor) for t in (q_t, k_t)):
-        raise ValueError("q_t and k_t must be Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
-    meta_q, meta_k = q.meta, k.meta
-    if v.meta.lengths != meta_k.lengths or q_t.meta.lengths != meta_q.lengths or k_t.meta.lengths != meta_k.lengths:
-        raise ValueError("operands disagree on sequence lengths")
-    if meta_q.num_seqs != meta_k.num_seqs:
-        raise ValueError("query and key metadata must have the same number of sequences")
-    for a, b in zip(meta_q.lengths, meta_k.lengths):
-        if a > 0 and b == 0:
-            raise ValueError("a sequence with queries needs keys")
-    for t, name in ((q.payload, "q"), (k.payload, "k"), (v.payload, "v"), (q_t.payload, "q_t"),
-                    (k_t.payload, "k_t"), (out, "out"), (dout, "dout")):
-        _check_rows(t, name)
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    tq, h = q.payload.shape[0], q.payload.shape[1]
-    tk = k.payload.shape[0]
-    dev = q.payload.device
-    for t, name, shape, dtype in ((out, "out", (tq, h, HEAD_DIM), torch.bfloat16),
-                                  (dout, "dout", (tq, h, HEAD_DIM), torch.bfloat16),
-                                  (lse, "lse", (h, tq), torch.float32)):
-        _check_out(t, shape, dtype, dev, name)
-    if softmax_scale is None:
-        softmax_scale = HEAD_DIM ** -0.5
-    delta = torch.empty((h, tq), dtype=torch.float32, device=dev)
-    dq = torch.empty((tq, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-    if output_mxfp8_dkv:
-        dk = torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev)
-        dv = torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev)
-        dks = torch.empty((meta_k.total_scale_rows, h, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
-        dvs = torch.empty((meta_k.total_scale_rows, h, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
-    else:
-        dk = torch.empty((tk, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-        dv = torch.empty((tk, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-        dks = dvs = None
-    a = _lib.BwdArgs()
-    a.struct_size = ctypes.sizeof(_lib.BwdArgs)
-    a.q, a.q_scale = _ptr(q.payload), _ptr(q.scales)
-    a.k, a.k_scale = _ptr(k.payload), _ptr(k.scales)
-    a.v, a.v_scale = _ptr(v.payload), _ptr(v.scales)
-    a.q_t, a.q_t_scale = _ptr(q_t.payload), _ptr(q_t.scales)
-    a.k_t, a.k_t_scale = _ptr(k_t.payload), _ptr(k_t.scales)
-    a.out, a.dout, a.lse = _ptr(out), _ptr(dout), _ptr(lse)
-    a.cu_seqlens_q, a.cu_seqlens_k = _ptr(meta_q.cu_seqlens), _ptr(meta_k.cu_seqlens)
-    a.cu_scale_q, a.cu_scale_k = _ptr(meta_q.cu_scale), _ptr(meta_k.cu_scale)
-    a.num_seqs, a.num_heads, a.head_dim, a.causal = meta_q.num_seqs, h, HEAD_DIM, 0
-    a.total_q, a.total_k = tq, tk
-    a.total_scale_rows_q, a.total_scale_rows_k = meta_q.total_scale_rows, meta_k.total_scale_rows
-    a.softmax_scale = float(softmax_scale)
-    a.output_mxfp8_dkv = 1 if output_mxfp8_dkv else 0
-    a.scaling_mode = _lib.SCALING[scaling_mode]
-    a.delta, a.dq, a.dk, a.dv = _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv)
-    a.dk_scale, a.dv_scale = _ptr(dks), _ptr(dvs)
-    lib = _lib.load()
-    _lib.check("lp_attn_varlen_bwd", lib.lp_attn_varlen_bwd(ctypes.byref(a), _stream()))
-    if output_mxfp8_dkv:
-        return dq, Mxfp8Tensor(dk, dks, meta_k), Mxfp8Tensor(dv, dvs, meta_k)
-    return dq, dk, dv
+    return BwdPlan(q, k, v, q_t, k_t, out, dout, lse, softmax_scale, output_mxfp8_dkv, scaling_mode)()

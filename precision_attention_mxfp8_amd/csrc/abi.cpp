@@ -191,13 +191,25 @@ int lp_attn_varlen_bwd(const lpfa_bwd_args* a, void* stream) {
   p.cu_k = a->cu_seqlens_k;
   p.cu_scale_q = a->cu_scale_q;
   p.cu_scale_k = a->cu_scale_k;
-  p.delta = a->delta;
+  {
+    // workspace: D, then BF16 copies of Qd, Qt, Kd, Vd, Kt (LPFA_BWD_WORK_BYTES)
+    uint8_t* w = static_cast<uint8_t*>(a->work);
+    const int64_t dbytes = ((int64_t)a->num_heads * a->total_q * 4 + 255) / 256 * 256;
+    const int64_t qb = (int64_t)a->num_heads * 256 * a->total_q, kb = (int64_t)a->num_heads * 256 * a->total_k;
+    p.delta = reinterpret_cast<float*>(w);
+    p.qd16 = reinterpret_cast<uint16_t*>(w + dbytes);
+    p.qt16 = reinterpret_cast<uint16_t*>(w + dbytes + qb);
+    p.kd16 = reinterpret_cast<uint16_t*>(w + dbytes + 2 * qb);
+    p.vd16 = reinterpret_cast<uint16_t*>(w + dbytes + 2 * qb + kb);
+    p.kt16 = reinterpret_cast<uint16_t*>(w + dbytes + 2 * qb + 2 * kb);
+  }
   p.dq = static_cast<uint16_t*>(a->dq);
   p.dk = static_cast<uint8_t*>(a->dk);
   p.dv = static_cast<uint8_t*>(a->dv);
   p.dk_scale = a->dk_scale;
   p.dv_scale = a->dv_scale;
   p.total_q = a->total_q;
+  p.total_k = a->total_k;
   // with no keys (or no queries) there is nothing to contract: only the other side's zero or
   // pad outputs are written
   p.rows_q = a->total_q > 0 ? a->total_scale_rows_q : 0;

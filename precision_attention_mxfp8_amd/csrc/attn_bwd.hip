@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -84,88 +86,46 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n, int row) {
   return lo;
 }
 
-// ---- staging: thread t moves row t/4, columns 32(t%4) .. +31 of a 64-row tile
-
-struct DRaw {  // head_dim orientation: 32 codes + their block's scale byte
-  uint4 a, b;
-  uint32_t sc;
-};
-struct TRaw {  // token orientation: 32 codes + one scale byte per column
-  uint4 a, b, s0, s1;
-};
-struct BRaw {  // 32 BF16
-  uint4 w[4];
-};
+// 4 codes of one word, each times its own column scale 2^(b - 127) (an exact ldexp) -> two BF16 pairs
+__device__ __forceinline__ uint2 fp8x4_colscaled(uint32_t w, uint32_t s) {
+  const float f0 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w, 0), (int)(s & 0xFFu) - 127);
+  const float f1 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w, 1), (int)((s >> 8) & 0xFFu) - 127);
+  const float f2 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w, 2), (int)((s >> 16) & 0xFFu) - 127);
+  const float f3 = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w, 3), (int)(s >> 24) - 127);
+  return make_uint2(cvt_pk_bf16(f0, f1), cvt_pk_bf16(f2, f3));
+}
 
 __device__ __forceinline__ LDS v4u_t* chunk_at(LDS uint8_t* tile, int r, int c) {
   return reinterpret_cast<LDS v4u_t*>(tile + r * 256 + ((c ^ (r & 15)) << 4));
 }
 
-__device__ __forceinline__ v4u_t vu(uint4 x) { return v4u_t{x.x, x.y, x.z, x.w}; }
-
-__device__ __forceinline__ DRaw load_d(const uint8_t* pay, const uint8_t* sc, int64_t tok, int64_t srow, int H,
-                                       int head, int c4) {
-  const uint4* src = reinterpret_cast<const uint4*>(pay + (tok * H + head) * 128 + 32 * c4);
-  DRaw d;
-  d.a = src[0];
-  d.b = src[1];
-  d.sc = sc[(srow * H + head) * 4 + c4];
-  return d;
+// Two floats -> two BF16 (nearest even) in one word, first in the low half (one conversion).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-__device__ __forceinline__ void store_d(LDS uint8_t* tile, int r, int c4, const DRaw& d) {
-  const float s = e8m0_f(d.sc);
-  *chunk_at(tile, r, 4 * c4 + 0) = vu(fp8x8_bf16(d.a.x, d.a.y, s));
-  *chunk_at(tile, r, 4 * c4 + 1) = vu(fp8x8_bf16(d.a.z, d.a.w, s));
-  *chunk_at(tile, r, 4 * c4 + 2) = vu(fp8x8_bf16(d.b.x, d.b.y, s));
-  *chunk_at(tile, r, 4 * c4 + 3) = vu(fp8x8_bf16(d.b.z, d.b.w, s));
-}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// tok: global token; tscale_row: row of the token-orientation scales (sequence offset / 32 +
-// the token's 32-block within the sequence)
-__device__ __forceinline__ TRaw load_t(const uint8_t* pay, const uint8_t* tsc, int64_t tok, int64_t tscale_row, int H,
-                                       int head, int c4) {
-  const uint4* src = reinterpret_cast<const uint4*>(pay + (tok * H + head) * 128 + 32 * c4);
-  const uint4* ssrc = reinterpret_cast<const uint4*>(tsc + (tscale_row * H + head) * 128 + 32 * c4);
-  TRaw t;
-  t.a = src[0];
-  t.b = src[1];
-  t.s0 = ssrc[0];
-  t.s1 = ssrc[1];
-  return t;
-}
-
-// 4 codes of one word, each times its own column scale -> two BF16 pairs
-__device__ __forceinline__ uint2 fp8x4_colscaled(uint32_t w, uint32_t s) {
-  const float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, 0) * e8m0_f(s & 0xFFu);
-  const float f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, 1) * e8m0_f((s >> 8) & 0xFFu);
-  const float f2 = __builtin_amdgcn_cvt_f32_fp8((int)w, 2) * e8m0_f((s >> 16) & 0xFFu);
-  const float f3 = __builtin_amdgcn_cvt_f32_fp8((int)w, 3) * e8m0_f(s >> 24);
-  return make_uint2(cvt_pk_bf16(f0, f1), cvt_pk_bf16(f2, f3));
-}
-
-__device__ __forceinline__ void store_t(LDS uint8_t* tile, int r, int c4, const TRaw& t) {
-  const uint32_t w[8] = {t.a.x, t.a.y, t.a.z, t.a.w, t.b.x, t.b.y, t.b.z, t.b.w};
-  const uint32_t s[8] = {t.s0.x, t.s0.y, t.s0.z, t.s0.w, t.s1.x, t.s1.y, t.s1.z, t.s1.w};
+// Stage a 64-row BF16 tile: rows tok0 + r (r clamped to nrows - 1) of head `head` of a
+// (tokens, H, 128) BF16 tensor ending at `end`; 16-byte chunk c of row r lands in LDS chunk
+// c ^ (r & 15). 16-byte direct-to-LDS loads fill 1 KB (4 rows) each in lane order, so lane L
+// fetches the global chunk that belongs at chunk position L % 16 of row L / 16. Wave w loads
+// rows 16w .. 16w + 15.
+__device__ __forceinline__ void stage_tile(LDS uint8_t* tile, const uint16_t* src, const uint16_t* end,
+                                           int64_t tok0, int nrows, int H, int head, int wave, int lane) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(src + (tok0 * H + head) * 128);
+  const int64_t left = reinterpret_cast<const uint8_t*>(end) - b;
+  const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(b), (short)0, n, 0x00020000);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint2 lo = fp8x4_colscaled(w[2 * m], s[2 * m]);
-    const uint2 hi = fp8x4_colscaled(w[2 * m + 1], s[2 * m + 1]);
-    *chunk_at(tile, r, 4 * c4 + m) = v4u_t{lo.x, lo.y, hi.x, hi.y};
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * i + (lane >> 4);
+    const int rc = min(r, nrows - 1);
+    const uint32_t off = (uint32_t)(rc * H * 256) + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(tile + (16 * wave + 4 * i) * 256), 16, off, 0, 0, 0);
   }
-}
-
-__device__ __forceinline__ BRaw load_b(const uint16_t* src, int64_t tok, int H, int head, int c4) {
-  const uint4* p = reinterpret_cast<const uint4*>(src + (tok * H + head) * 128 + 32 * c4);
-  BRaw b;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) b.w[m] = p[m];
-  return b;
-}
-
-__device__ __forceinline__ void store_b(LDS uint8_t* tile, int r, int c4, const BRaw& b) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m) *chunk_at(tile, r, 4 * c4 + m) = vu(b.w[m]);
 }
 
 // ---- operand reads
@@ -191,6 +151,45 @@ __device__ __forceinline__ v8bf col_frag(LDS uint8_t* tile, int s, int dt, int g
 
 __device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Ends a scheduling group: the fragment reads written before it are issued together, and the
+// matrix instructions that use them follow (one wait for the group instead of one per read).
+__device__ __forceinline__ void group_end() { __builtin_amdgcn_sched_barrier(0); }
+
+// ---- pre-pass: each MX operand dequantized once into a BF16 copy (tokens, H, 128)
+// blockIdx.y selects the tensor: 0 Qd, 1 Qt, 2 Kd, 3 Vd, 4 Kt (t: token orientation). A thread
+// converts one 8-element chunk of a padded scale row; pad rows have no tokens and are skipped.
+__global__ __launch_bounds__(256) void bwd_dequant_kernel(BwdParams p) {
+  const int job = blockIdx.y;
+  const bool isq = job < 2, tok_orient = job == 1 || job == 4;
+  const uint8_t* pay = job == 0 ? p.q : job == 1 ? p.q_t : job == 2 ? p.k : job == 3 ? p.v : p.k_t;
+  const uint8_t* sc = job == 0 ? p.q_scale : job == 1 ? p.q_t_scale : job == 2 ? p.k_scale : job == 3 ? p.v_scale : p.k_t_scale;
+  uint16_t* dst = job == 0 ? p.qd16 : job == 1 ? p.qt16 : job == 2 ? p.kd16 : job == 3 ? p.vd16 : p.kt16;
+  const int32_t* cu = isq ? p.cu_q : p.cu_k;
+  const int32_t* cs = isq ? p.cu_scale_q : p.cu_scale_k;
+  const int64_t rows = isq ? p.rows_q : p.rows_k;
+  const int H = p.num_heads;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t srow = gid / (H * 16);
+  if (srow >= rows) return;
+  const int rem = (int)(gid - srow * H * 16);
+  const int head = rem >> 4, c = rem & 15;
+  const int seq = find_seq(cs, p.num_seqs, (int)srow);
+  const int local = (int)srow - cs[seq];
+  if (local >= cu[seq + 1] - cu[seq]) return;  // pad row
+  const int64_t off = (((int64_t)cu[seq] + local) * H + head) * 128 + 8 * c;
+  const uint2 w = *reinterpret_cast<const uint2*>(pay + off);
+  uint4 out;
+  if (!tok_orient) {
+    out = fp8x8_bf16(w.x, w.y, e8m0_f(sc[(srow * H + head) * 4 + (c >> 2)]));
+  } else {
+    const int64_t trow = cs[seq] / 32 + local / 32;
+    const uint2 sw = *reinterpret_cast<const uint2*>(sc + (trow * H + head) * 128 + 8 * c);
+    const uint2 lo = fp8x4_colscaled(w.x, sw.x), hi = fp8x4_colscaled(w.y, sw.y);
+    out = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  *reinterpret_cast<uint4*>(dst + off) = out;
 }
 
 // ---- D = rowsum(dO * O)
@@ -236,8 +235,8 @@ __device__ __forceinline__ void emit_rows(LDS float* ep, uint8_t* dst, uint8_t* 
       uint4* d = reinterpret_cast<uint4*>(dst + off * 2);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        d[m] = make_uint4(cvt_pk_bf16(v[8 * m], v[8 * m + 1]), cvt_pk_bf16(v[8 * m + 2], v[8 * m + 3]),
-                          cvt_pk_bf16(v[8 * m + 4], v[8 * m + 5]), cvt_pk_bf16(v[8 * m + 6], v[8 * m + 7]));
+        d[m] = make_uint4(pk_bf16(v[8 * m], v[8 * m + 1]), pk_bf16(v[8 * m + 2], v[8 * m + 3]),
+                          pk_bf16(v[8 * m + 4], v[8 * m + 5]), pk_bf16(v[8 * m + 6], v[8 * m + 7]));
     }
     return;
   }
@@ -291,7 +290,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
-  const int r = tid >> 2, c4 = tid & 3;
 
   v4f dv[8], dk[8];
 #pragma unroll
@@ -318,45 +316,39 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     const float c = p.softmax_scale * LOG2E;
     const int nqb = (Lq + BR - 1) / BR;
 
-    DRaw rq;
-    BRaw rdo;
-    TRaw rqt;
-    float rl2 = 0.0f, rdl = 0.0f;
-    auto load_step = [&](int j) {
-      const int qr = min(j * BR + r, Lq - 1);
-      const int64_t tq_ = qbase + qr;
-      rq = load_d(p.q, p.q_scale, tq_, srow_q + qr, H, head, c4);
-      rdo = load_b(p.dout, tq_, H, head, c4);
-      rqt = load_t(p.q_t, p.q_t_scale, tq_, srow_q / 32 + qr / 32, H, head, c4);
+    const int64_t qelems = p.total_q * H * 128;
+    for (int j = 0; j < nqb; ++j) {
+      const int64_t t0 = qbase + (int64_t)j * BR;
+      const int nr = Lq - j * BR;
+      stage_tile(tq, p.qd16, p.qd16 + qelems, t0, nr, H, head, wave, lane);
+      stage_tile(tdo, p.dout, p.dout + qelems, t0, nr, H, head, wave, lane);
+      stage_tile(tqt, p.qt16, p.qt16 + qelems, t0, nr, H, head, wave, lane);
       if (tid < BR) {
         const int qv = j * BR + tid;
         const int64_t t2 = qbase + min(qv, Lq - 1);
-        rl2 = qv < Lq ? p.lse[(int64_t)head * p.total_q + t2] * LOG2E : __builtin_inff();
-        rdl = qv < Lq ? p.delta[(int64_t)head * p.total_q + t2] : 0.0f;
+        vec[tid] = qv < Lq ? p.lse[(int64_t)head * p.total_q + t2] * LOG2E : __builtin_inff();
+        vec[BR + tid] = qv < Lq ? p.delta[(int64_t)head * p.total_q + t2] : 0.0f;
       }
-    };
-    load_step(0);
-    for (int j = 0; j < nqb; ++j) {
-      store_d(tq, r, c4, rq);
-      store_b(tdo, r, c4, rdo);
-      store_t(tqt, r, c4, rqt);
-      if (tid < BR) {
-        vec[tid] = rl2;
-        vec[BR + tid] = rdl;
-      }
+      wait_vm_all();
       __syncthreads();
-      if (j + 1 < nqb) load_step(j + 1);
 
       // S and dP: lane (g, n16) holds key n16 of the wave, queries 16qt + 4g + i
       v4f s[4], dp[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
+        v8bf aq[4], ao[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          aq[u] = row_frag(tq, 16 * qt + n16, 4 * u + g);
+          ao[u] = row_frag(tdo, 16 * qt + n16, 4 * u + g);
+        }
         s[qt] = dp[qt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          s[qt] = mfma(row_frag(tq, 16 * qt + n16, 4 * u + g), kf[u], s[qt]);
-          dp[qt] = mfma(row_frag(tdo, 16 * qt + n16, 4 * u + g), vf[u], dp[qt]);
+          s[qt] = mfma(aq[u], kf[u], s[qt]);
+          dp[qt] = mfma(ao[u], vf[u], dp[qt]);
         }
+        group_end();
       }
       uint32_t pw[2][4], dw[2][4];
 #pragma unroll
@@ -369,19 +361,29 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           pr[i] = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c, -lv[i]));
           ds[i] = pr[i] * (dp[qt][i] - dv4[i]);
         }
-        pw[qt >> 1][2 * (qt & 1)] = cvt_pk_bf16(pr[0], pr[1]);
-        pw[qt >> 1][2 * (qt & 1) + 1] = cvt_pk_bf16(pr[2], pr[3]);
-        dw[qt >> 1][2 * (qt & 1)] = cvt_pk_bf16(ds[0], ds[1]);
-        dw[qt >> 1][2 * (qt & 1) + 1] = cvt_pk_bf16(ds[2], ds[3]);
+        pw[qt >> 1][2 * (qt & 1)] = pk_bf16(pr[0], pr[1]);
+        pw[qt >> 1][2 * (qt & 1) + 1] = pk_bf16(pr[2], pr[3]);
+        dw[qt >> 1][2 * (qt & 1)] = pk_bf16(ds[0], ds[1]);
+        dw[qt >> 1][2 * (qt & 1) + 1] = pk_bf16(ds[2], ds[3]);
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const v8bf ap = __builtin_bit_cast(v8bf, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
         const v8bf ad = __builtin_bit_cast(v8bf, make_uint4(dw[st][0], dw[st][1], dw[st][2], dw[st][3]));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          dv[dt] = mfma(ap, col_frag(tdo, st, dt, g, n16), dv[dt]);
-          dk[dt] = mfma(ad, col_frag(tqt, st, dt, g, n16), dk[dt]);
+        for (int d0 = 0; d0 < 8; d0 += 4) {
+          v8bf bo[4], bq[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bo[i] = col_frag(tdo, st, d0 + i, g, n16);
+            bq[i] = col_frag(tqt, st, d0 + i, g, n16);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dv[d0 + i] = mfma(ap, bo[i], dv[d0 + i]);
+            dk[d0 + i] = mfma(ad, bq[i], dk[d0 + i]);
+          }
+          group_end();
         }
       }
       __syncthreads();
@@ -419,7 +421,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
-  const int r = tid >> 2, c4 = tid & 3;
 
   v4f dq[8];
 #pragma unroll
@@ -447,52 +448,63 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const float c = p.softmax_scale * LOG2E;
     const int nkb = (Lk + BR - 1) / BR;
 
-    DRaw rk, rv;
-    TRaw rkt;
-    auto load_step = [&](int j) {
-      const int kr = min(j * BR + r, Lk - 1);
-      const int64_t t = kbase + kr;
-      rk = load_d(p.k, p.k_scale, t, srow_k + kr, H, head, c4);
-      rv = load_d(p.v, p.v_scale, t, srow_k + kr, H, head, c4);
-      rkt = load_t(p.k_t, p.k_t_scale, t, srow_k / 32 + kr / 32, H, head, c4);
-    };
-    load_step(0);
+    const int64_t kelems = p.total_k * H * 128;
     for (int j = 0; j < nkb; ++j) {
-      store_d(tk, r, c4, rk);
-      store_d(tv, r, c4, rv);
-      store_t(tkt, r, c4, rkt);
+      const int64_t t0 = kbase + (int64_t)j * BR;
+      const int nr = Lk - j * BR;
+      stage_tile(tk, p.kd16, p.kd16 + kelems, t0, nr, H, head, wave, lane);
+      stage_tile(tv, p.vd16, p.vd16 + kelems, t0, nr, H, head, wave, lane);
+      stage_tile(tkt, p.kt16, p.kt16 + kelems, t0, nr, H, head, wave, lane);
+      wait_vm_all();
       __syncthreads();
-      if (j + 1 < nkb) load_step(j + 1);
 
       // S^T and dP^T: lane (g, n16) holds query n16 of the wave, keys 16kt + 4g + i
       v4f s[4], dp[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
+        v8bf ak[4], av[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ak[u] = row_frag(tk, 16 * kt + n16, 4 * u + g);
+          av[u] = row_frag(tv, 16 * kt + n16, 4 * u + g);
+        }
         s[kt] = dp[kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          s[kt] = mfma(row_frag(tk, 16 * kt + n16, 4 * u + g), qf[u], s[kt]);
-          dp[kt] = mfma(row_frag(tv, 16 * kt + n16, 4 * u + g), of[u], dp[kt]);
+          s[kt] = mfma(ak[u], qf[u], s[kt]);
+          dp[kt] = mfma(av[u], of[u], dp[kt]);
         }
+        group_end();
       }
       uint32_t dw[2][4];
+      auto scores_to_ds = [&](auto masked) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float ds[4];
+        for (int kt = 0; kt < 4; ++kt) {
+          float ds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool kin = j * BR + 16 * kt + 4 * g + i < Lk;
-          const float pr = kin ? __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -l2)) : 0.0f;
-          ds[i] = pr * (dp[kt][i] - dl);
+          for (int i = 0; i < 4; ++i) {
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -l2));
+            if constexpr (decltype(masked)::value) pr = 16 * kt + 4 * g + i < nr ? pr : 0.0f;
+            ds[i] = pr * (dp[kt][i] - dl);
+          }
+          dw[kt >> 1][2 * (kt & 1)] = pk_bf16(ds[0], ds[1]);
+          dw[kt >> 1][2 * (kt & 1) + 1] = pk_bf16(ds[2], ds[3]);
         }
-        dw[kt >> 1][2 * (kt & 1)] = cvt_pk_bf16(ds[0], ds[1]);
-        dw[kt >> 1][2 * (kt & 1) + 1] = cvt_pk_bf16(ds[2], ds[3]);
-      }
+      };
+      if (nr >= BR) scores_to_ds(std::false_type{});  // a full block: no key mask
+      else scores_to_ds(std::true_type{});
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const v8bf ad = __builtin_bit_cast(v8bf, make_uint4(dw[st][0], dw[st][1], dw[st][2], dw[st][3]));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) dq[dt] = mfma(ad, col_frag(tkt, st, dt, g, n16), dq[dt]);
+        for (int d0 = 0; d0 < 8; d0 += 4) {
+          v8bf bk[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bk[i] = col_frag(tkt, st, d0 + i, g, n16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dq[d0 + i] = mfma(ad, bk[i], dq[d0 + i]);
+          group_end();
+        }
       }
       __syncthreads();
     }
@@ -507,6 +519,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 }  // namespace
 
 hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s) {
+  const int64_t jobs_rows = p.rows_q > p.rows_k ? p.rows_q : p.rows_k;
+  if (p.rows_q > 0 && p.rows_k > 0)
+    hipLaunchKernelGGL(bwd_dequant_kernel, dim3((unsigned)((jobs_rows * p.num_heads * 16 + 255) / 256), 5), dim3(256), 0,
+                       s, p);
   const int64_t rows = p.total_q * p.num_heads;
   if (rows > 0)
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, p);

@@ -83,13 +83,20 @@ struct BwdParams {
   const int32_t* cu_k;
   const int32_t* cu_scale_q;
   const int32_t* cu_scale_k;
-  float* delta;  // (H, total_q)
+  float* delta;  // (H, total_q), in the workspace
+  // BF16 copies in the workspace (tokens, H, 128): Q and K in both orientations, V along head_dim
+  uint16_t* qd16;
+  uint16_t* qt16;
+  uint16_t* kd16;
+  uint16_t* vd16;
+  uint16_t* kt16;
   uint16_t* dq;
   uint8_t* dk;   // BF16 bytes or E4M3 payload
   uint8_t* dv;
   uint8_t* dk_scale;
   uint8_t* dv_scale;
   int64_t total_q;
+  int64_t total_k;
   int64_t rows_q;  // total scale rows of Q and K (multiples of 128)
   int64_t rows_k;
   int32_t num_seqs;

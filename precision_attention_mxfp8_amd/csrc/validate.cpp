@@ -202,7 +202,7 @@ int check_bwd(const lpfa_bwd_args* a) {
       {a->q_t, both, "q_t", 16u},       {a->q_t_scale, both, "q_t_scale", 16u},
       {a->k_t, both, "k_t", 16u},       {a->k_t_scale, both, "k_t_scale", 16u},
       {a->out, hq, "out", 16u},         {a->dout, hq, "dout", 16u},
-      {a->lse, both, "lse", 4u},        {a->delta, hq, "delta", 4u},
+      {a->lse, both, "lse", 4u},        {a->work, hq || hk, "work", 256u},
       {a->dq, hq, "dq", 16u},           {a->dk, hk, "dk", 16u},
       {a->dv, hk, "dv", 16u},
   };

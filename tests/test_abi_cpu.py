@@ -192,7 +192,7 @@ def _bwd_args(**kw):
     a = _lib.BwdArgs()
     a.struct_size = ctypes.sizeof(_lib.BwdArgs)
     for f in ("q", "q_scale", "k", "k_scale", "v", "v_scale", "q_t", "q_t_scale", "k_t", "k_t_scale", "out",
-              "dout", "lse", "cu_seqlens_q", "cu_seqlens_k", "cu_scale_q", "cu_scale_k", "delta", "dq", "dk", "dv"):
+              "dout", "lse", "cu_seqlens_q", "cu_seqlens_k", "cu_scale_q", "cu_scale_k", "work", "dq", "dk", "dv"):
         setattr(a, f, FAKE)
     a.num_seqs, a.num_heads, a.head_dim = 1, 2, 128
     a.total_q = a.total_k = 100
@@ -220,7 +220,8 @@ def _bwd_args(**kw):
     (dict(k_t_scale=FAKE + 4), _lib.LPFA_EINVAL),         # token scales are read 16 bytes at a time
     (dict(dq=FAKE + 2), _lib.LPFA_EINVAL),
     (dict(lse=FAKE + 2), _lib.LPFA_EINVAL),
-    (dict(delta=None), _lib.LPFA_EINVAL),
+    (dict(work=None), _lib.LPFA_EINVAL),
+    (dict(work=FAKE + 16), _lib.LPFA_EINVAL),             # the workspace is 256-byte aligned
     (dict(cu_scale_k=None), _lib.LPFA_EINVAL),
     (dict(num_seqs=0), _lib.LPFA_EINVAL),                 # tokens without sequences
 ])
