@@ -56,6 +56,20 @@ def test_struct_layout_matches_c(cname, pystruct):
         assert int(got[f]) == getattr(pystruct, f).offset, f
 
 
+@pytest.mark.parametrize("tq,tk,h", [(0, 0, 1), (2048, 2048, 16), (4096, 32768, 16), (5, 7, 3)])
+def test_backward_workspace_macro_matches_python(tq, tk, h):
+    src = ['#include <stdio.h>', '#include "lpfa.h"', "int main(void){",
+           f'printf("%lld\\n", (long long)LPFA_BWD_WORK_BYTES({tq}, {tk}, {h}));', "return 0;}"]
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "w.c")
+        exe = os.path.join(d, "w")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = int(subprocess.run([exe], capture_output=True, text=True, check=True).stdout)
+    assert got == _lib.bwd_work_bytes(tq, tk, h)
+    assert got % 256 == 0
+
+
 FAKE = 0x10000  # an aligned non-NULL address: validation checks it, nothing dereferences it
 
 
