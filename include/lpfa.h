@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 5
+#define LPFA_ABI_VERSION 6
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -141,6 +141,26 @@ int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok,
 int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                      int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
                      void* stream);
+
+/*
+ * mxfp8_prepare_qkv - the forward's three preparation passes in one launch: Q and K as
+ * mxfp8_quantize_varlen (K with its group maxima) and V as lp_fp8_cast_e4m3 (the fp8 PV mode).
+ * (LP-FA4 README, section "MXFP8 forward and backward"; FastVideo fp8-PV PR: unscaled V cast.)
+ *
+ * The outputs are byte-identical to the three separate calls; only the launch is shared. q, k
+ * and v have one dtype (x_dtype) and the same token and head strides (elements); total_q and
+ * total_k are their token counts (v has total_k). The metadata, payload, scale and group-max
+ * arguments mean what they mean for mxfp8_quantize_varlen (k_group_max may be NULL); v_codes is
+ * uint8 (total_k, num_heads, 128) contiguous.
+ * Errors: those of the three separate calls.
+ */
+int mxfp8_prepare_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t stride_tok,
+                      int64_t stride_head, int64_t total_q, int64_t total_k, int32_t num_heads,
+                      int32_t head_dim, const int32_t* cu_seqlens_q, const int32_t* cu_scale_q,
+                      const int32_t* cu_seqlens_k, const int32_t* cu_scale_k, int32_t num_seqs,
+                      int64_t total_scale_rows_q, int64_t total_scale_rows_k, int scaling_mode,
+                      uint8_t* q_payload, uint8_t* q_scales, uint8_t* k_payload, uint8_t* k_scales,
+                      uint8_t* k_group_max, uint8_t* v_codes, void* stream);
 
 /*
  * lp_fp8_cast_current - per-tensor current scaling to E4M3.

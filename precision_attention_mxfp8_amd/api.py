@@ -199,6 +199,55 @@ def quantize_mxfp8_varlen_tokens(x: torch.Tensor, meta: VarlenMeta, scaling_mode
     return out
 
 
+def prepare_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta_q: VarlenMeta, meta_k: VarlenMeta,
+                scaling_mode: str = "rceil",
+                out: Optional[Tuple[Mxfp8Tensor, Mxfp8Tensor, torch.Tensor]] = None
+                ) -> Tuple[Mxfp8Tensor, Mxfp8Tensor, torch.Tensor]:
+    """The fp8-PV forward's preparation in one launch: (quantize_mxfp8_varlen(q), quantize_mxfp8_varlen(k)
+    with group maxima, cast_e4m3(v)), byte-identical to the three calls. q, k, v share dtype and
+    strides. ``out``: (q_mx, k_mx, v_codes) buffers to write into."""
+    mode = _lib.SCALING.get(scaling_mode)
+    if mode is None:
+        raise ValueError(f"scaling_mode must be one of {sorted(_lib.SCALING)}, got {scaling_mode!r}")
+    dt = _fp_input(q)
+    for t, name in ((k, "k"), (v, "v")):
+        _check_rows(t, name)
+        if t.dtype != q.dtype or t.stride()[:2] != q.stride()[:2]:
+            raise ValueError(f"{name} must have q's dtype and strides")
+    tq, h, _ = q.shape
+    tk = k.shape[0]
+    if tq != meta_q.total_tokens or tk != meta_k.total_tokens or v.shape[0] != tk or k.shape[1] != h or v.shape[1] != h:
+        raise ValueError("q, k, v shapes disagree with the metadata")
+    if meta_q.num_seqs != meta_k.num_seqs:
+        raise ValueError("query and key metadata must have the same number of sequences")
+    dev = q.device
+    if out is None:
+        qo = Mxfp8Tensor(torch.empty((tq, h, HEAD_DIM), dtype=torch.uint8, device=dev),
+                         torch.empty((meta_q.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), meta_q)
+        ko = Mxfp8Tensor(torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev),
+                         torch.empty((meta_k.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), meta_k,
+                         torch.empty((meta_k.total_scale_rows // 16, h), dtype=torch.uint8, device=dev))
+        vo = torch.empty((tk, h, HEAD_DIM), dtype=torch.uint8, device=dev)
+    else:
+        qo, ko, vo = out
+        _check_out(qo.payload, (tq, h, HEAD_DIM), torch.uint8, dev, "q payload")
+        _check_out(qo.scales, (meta_q.total_scale_rows, h, 4), torch.uint8, dev, "q scales")
+        _check_out(ko.payload, (tk, h, HEAD_DIM), torch.uint8, dev, "k payload")
+        _check_out(ko.scales, (meta_k.total_scale_rows, h, 4), torch.uint8, dev, "k scales")
+        if ko.group_max is not None:
+            _check_out(ko.group_max, (meta_k.total_scale_rows // 16, h), torch.uint8, dev, "k group_max")
+        _check_out(vo, (tk, h, HEAD_DIM), torch.uint8, dev, "v codes")
+    rc = _lib.load().mxfp8_prepare_qkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, q.stride(0), q.stride(1), tq, tk, h, HEAD_DIM,
+        meta_q.cu_seqlens.data_ptr(), meta_q.cu_scale.data_ptr(), meta_k.cu_seqlens.data_ptr(),
+        meta_k.cu_scale.data_ptr(), meta_q.num_seqs, meta_q.total_scale_rows, meta_k.total_scale_rows, mode,
+        qo.payload.data_ptr(), qo.scales.data_ptr(), ko.payload.data_ptr(), ko.scales.data_ptr(),
+        None if ko.group_max is None else ko.group_max.data_ptr(), vo.data_ptr(), _stream())
+    if rc:
+        _lib.check("mxfp8_prepare_qkv", rc)
+    return qo, ko, vo
+
+
 def cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Unscaled E4M3 cast (fp8 PV mode's V): uint8 codes, same (tokens, heads, 128) shape, contiguous.
 

@@ -75,6 +75,56 @@ int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok,
   return launch_status(lpfa::launch_quantize_tokens(p, static_cast<hipStream_t>(stream)), "token quantize");
 }
 
+int mxfp8_prepare_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t stride_tok,
+                      int64_t stride_head, int64_t total_q, int64_t total_k, int32_t num_heads,
+                      int32_t head_dim, const int32_t* cu_seqlens_q, const int32_t* cu_scale_q,
+                      const int32_t* cu_seqlens_k, const int32_t* cu_scale_k, int32_t num_seqs,
+                      int64_t total_scale_rows_q, int64_t total_scale_rows_k, int scaling_mode,
+                      uint8_t* q_payload, uint8_t* q_scales, uint8_t* k_payload, uint8_t* k_scales,
+                      uint8_t* k_group_max, uint8_t* v_codes, void* stream) {
+  if (int rc = lpfa::check_quantize(q, x_dtype, stride_tok, stride_head, total_q, num_heads, head_dim,
+                                    cu_seqlens_q, cu_scale_q, num_seqs, total_scale_rows_q, scaling_mode,
+                                    q_payload, q_scales))
+    return rc;
+  if (int rc = lpfa::check_quantize(k, x_dtype, stride_tok, stride_head, total_k, num_heads, head_dim,
+                                    cu_seqlens_k, cu_scale_k, num_seqs, total_scale_rows_k, scaling_mode,
+                                    k_payload, k_scales))
+    return rc;
+  if (int rc = lpfa::check_cast(v, x_dtype, stride_tok, stride_head, total_k, num_heads, head_dim, v_codes))
+    return rc;
+  lpfa::QuantParams pq{}, pk{};
+  for (lpfa::QuantParams* p : {&pq, &pk}) {
+    p->x_dtype = x_dtype;
+    p->scaling_mode = scaling_mode;
+    p->stride_tok = stride_tok;
+    p->stride_head = stride_head;
+    p->num_heads = num_heads;
+    p->num_seqs = num_seqs;
+  }
+  pq.x = q;
+  pq.total_scale_rows = total_scale_rows_q;
+  pq.cu_seqlens = cu_seqlens_q;
+  pq.cu_scale = cu_scale_q;
+  pq.payload = q_payload;
+  pq.scales = q_scales;
+  pk.x = k;
+  pk.total_scale_rows = total_scale_rows_k;
+  pk.cu_seqlens = cu_seqlens_k;
+  pk.cu_scale = cu_scale_k;
+  pk.payload = k_payload;
+  pk.scales = k_scales;
+  pk.group_max = k_group_max;
+  lpfa::CastParams pv{};
+  pv.x = v;
+  pv.x_dtype = x_dtype;
+  pv.stride_tok = stride_tok;
+  pv.stride_head = stride_head;
+  pv.total_tokens = total_k;
+  pv.num_heads = num_heads;
+  pv.y = v_codes;
+  return launch_status(lpfa::launch_prepare_qkv(pq, pk, pv, static_cast<hipStream_t>(stream)), "prepare");
+}
+
 int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                      int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
                      void* stream) {

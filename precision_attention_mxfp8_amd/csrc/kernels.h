@@ -109,6 +109,8 @@ struct BwdParams {
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s);  // scales: token orientation
 hipError_t launch_cast(const CastParams& p, hipStream_t s);
+hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, const CastParams& pv,
+                              hipStream_t s);  // quantize Q, K and cast V in one launch (one dtype)
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s);  // amax, then E4M3(x / s)
 hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

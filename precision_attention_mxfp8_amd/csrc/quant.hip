@@ -54,11 +54,12 @@ struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
   }
 };
 
+// One workgroup's share of the quantizer: 16 rows of the scale storage for one head (`bid`
+// enumerates (16-row group, head) pairs, heads fastest).
 template <typename T>
-__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
-  __shared__ uint32_t red[4];
-  const int h = (int)(blockIdx.x % (unsigned)p.num_heads);  // neighbouring workgroups: same rows
-  const int64_t grp16 = blockIdx.x / (unsigned)p.num_heads;  // 16-row group of the scale storage
+__device__ __forceinline__ void quantize_group(const QuantParams& p, unsigned bid, uint32_t* red) {
+  const int h = (int)(bid % (unsigned)p.num_heads);  // neighbouring workgroups: same rows
+  const int64_t grp16 = bid / (unsigned)p.num_heads;  // 16-row group of the scale storage
   const int sub = threadIdx.x & 15;                           // 8-element chunk of the 128-element row
   const int64_t srow = grp16 * 16 + (threadIdx.x >> 4);
 
@@ -111,6 +112,12 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
     if (threadIdx.x == 0)
       p.group_max[grp16 * p.num_heads + h] = (uint8_t)max(max(red[0], red[1]), max(red[2], red[3]));
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
+  __shared__ uint32_t red[4];
+  quantize_group<T>(p, blockIdx.x, red);
 }
 
 // Loads 4 consecutive elements (8 bytes BF16, 16 bytes FP32) as floats.
@@ -198,8 +205,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_tokens_kernel(QuantParams 
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
+  const int64_t gid = (int64_t)bid * 256 + threadIdx.x;
   const int64_t head_row = gid >> 4;
   const int sub = threadIdx.x & 15;
   if (head_row >= p.total_tokens * p.num_heads) return;
@@ -210,6 +217,25 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
   uint32_t w0 = cvt4_e4m3(clamp448(v[0]), clamp448(v[1]), clamp448(v[2]), clamp448(v[3]));
   uint32_t w1 = cvt4_e4m3(clamp448(v[4]), clamp448(v[5]), clamp448(v[6]), clamp448(v[7]));
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
+  cast_block<T>(p, blockIdx.x);
+}
+
+// The three preparation passes of a forward in one launch: Q's and K's MXFP8 quantization and
+// V's unscaled E4M3 cast. Each of these passes moves ~12 MB at the dense shape, too little for
+// one launch to get past its ramp-up and tail; one grid over all three amortizes them. Workgroup
+// ranges: [0, nq) Q, [nq, nq + nk) K, then V; each workgroup runs one pass's body unchanged.
+template <typename T>
+__global__ __launch_bounds__(256) void prepare_qkv_kernel(QuantParams pq, QuantParams pk, CastParams pv, unsigned nq,
+                                                          unsigned nk) {
+  __shared__ uint32_t red[4];
+  const unsigned b = blockIdx.x;
+  if (b < nq) quantize_group<T>(pq, b, red);
+  else if (b < nq + nk) quantize_group<T>(pk, b - nq, red);
+  else cast_block<T>(pv, b - nq - nk);
 }
 
 // ---- per-tensor current scaling (TensorRT-LLM TE-backend PR: Q/K/V and O scales written from
@@ -319,6 +345,18 @@ hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s) {
     hipLaunchKernelGGL(mxfp8_quantize_tokens_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(mxfp8_quantize_tokens_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, const CastParams& pv, hipStream_t s) {
+  const int64_t nq = pq.total_scale_rows / 16 * pq.num_heads, nk = pk.total_scale_rows / 16 * pk.num_heads;
+  const int64_t nv = (pv.total_tokens * pv.num_heads * 16 + 255) / 256;
+  if (nq + nk + nv == 0) return hipSuccess;
+  const dim3 grid((unsigned)(nq + nk + nv));
+  if (pq.x_dtype == LPFA_DTYPE_BF16)
+    hipLaunchKernelGGL(prepare_qkv_kernel<uint16_t>, grid, dim3(256), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
+  else
+    hipLaunchKernelGGL(prepare_qkv_kernel<float>, grid, dim3(256), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 5
+    assert lib.lpfa_abi_version() == 6
 
 
 @pytest.mark.parametrize("cname,pystruct", [("lpfa_attn_args", _lib.AttnArgs), ("lpfa_bwd_args", _lib.BwdArgs)])
@@ -133,6 +133,25 @@ def test_cast_current_rejects(lib):
     assert f(FAKE, 0, 256, 128, 2, 2, 128, FAKE + 2, FAKE, FAKE, None) == _lib.LPFA_EINVAL
     assert f(FAKE, 3, 256, 128, 2, 2, 128, FAKE, FAKE, FAKE, None) == _lib.LPFA_EINVAL     # dtype
     assert f(FAKE, 0, 256, 128, 2, 2, 128, FAKE, None, FAKE, None) == _lib.LPFA_EINVAL     # y
+    assert lib.lpfa_last_error().decode()
+
+
+def test_prepare_rejects(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=0, st=256, sh=128, tq=2, tk=2, h=2, d=128, cuq=FAKE, csq=FAKE,
+                 cuk=FAKE, csk=FAKE, n=1, rq=128, rk=128, mode=0, qp=FAKE, qs=FAKE, kp=FAKE, ks=FAKE, kg=None,
+                 vc=FAKE)
+        a.update(kw)
+        return lib.mxfp8_prepare_qkv(*a.values(), None)
+    assert call(d=64) == _lib.LPFA_ENOTSUP
+    assert call(mode=2) == _lib.LPFA_EINVAL
+    assert call(dt=5) == _lib.LPFA_EINVAL
+    assert call(qs=None) == _lib.LPFA_EINVAL
+    assert call(ks=None) == _lib.LPFA_EINVAL
+    assert call(csk=None) == _lib.LPFA_EINVAL
+    assert call(vc=None) == _lib.LPFA_EINVAL
+    assert call(v=FAKE + 8) == _lib.LPFA_EINVAL
+    assert call(st=100) == _lib.LPFA_EINVAL
     assert lib.lpfa_last_error().decode()
 
 
