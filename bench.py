@@ -125,7 +125,7 @@ def main():
     vx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev) if pv_mode == "fp8" else v
     plan = lp.AttnPlan(mq, mk, h, pv_mode=pv_mode, mx=not per_tensor, tile_order=order)
     out, lse = plan.out, plan.lse
-    state = {}
+    state = {"fence": torch.cuda.Event()}
 
     fused_prep = not per_tensor and pv_mode == "fp8" and not args.separate_prep
 
@@ -141,7 +141,11 @@ def main():
                 lp.quantize_mxfp8_varlen(k, mk, out=kx)
             if pv_mode == "fp8":
                 lp.cast_e4m3(v, out=vx)
-        # in the timed region the kernel's own dispatch stamps a (start, stop) event pair
+        # in the timed region the kernel's own dispatch stamps a (start, stop) event pair; a plain
+        # event recorded first makes the queue finish the preparation before it picks up the
+        # stamped dispatch, so the start stamp is not taken while the preparation still drains
+        if state.get("ev") is not None:
+            state["fence"].record()
         plan(qx, kx, vx, timing=state.get("ev"))
 
     log(f"workload {args.workload} pv_mode {pv_mode}: {flops / 1e9:.2f} GFLOP per forward")
