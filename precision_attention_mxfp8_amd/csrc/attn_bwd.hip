@@ -11,6 +11,8 @@
 // 32-element blocks run along its contraction). P and dS enter the products rounded to BF16.
 //
 // Kernels (in stream order)
+//  * bwd_dequant_kernel: Qd, Qt, Kd, Vd and Kt dequantized once into BF16 copies in the caller's
+//    workspace (the main kernels re-read every tile once per 64-row block of the other side).
 //  * bwd_delta_kernel: D for every (head, query) into the caller's workspace; 16 lanes per row.
 //  * bwd_dkdv_kernel: one workgroup = (64 keys of one sequence, head), 4 waves x 16 keys. The
 //    keys' K and V fragments and the dK, dV accumulators stay in registers while the workgroup
@@ -21,8 +23,8 @@
 //    of scheduling; the price is recomputing S and dP.
 //
 // Matrix instruction: v_mfma_f32_16x16x32_bf16 everywhere, on operands dequantized into BF16
-// while they are staged (an E4M3 code times 2^e has at most 4 significant bits, so the BF16
-// value is exact inside BF16's normal range). The scores are recomputed from these exact
+// (an E4M3 code times 2^e has at most 4 significant bits, so the BF16 value is exact inside
+// BF16's normal range). The scores are recomputed from these exact
 // operands in FP32. Layouts (A lane (g, r): row r, k = 8g..8g+7; B lane (g, c): column c, the
 // same k; result lane (g, c): column c, rows 4g..4g+3):
 //  * dK/dV pass: S = Q K^T and dP = dO V^T with queries as rows, so lane (g, n) holds key n and
@@ -34,8 +36,9 @@
 //    4g+i, the A operand of dQ = dS Kt under the same map; Kt by column through transposing reads.
 // LDS tiles are 64 rows x 128 BF16 (256-byte rows) with 16-byte chunk c of row r stored at
 // chunk c ^ (r & 15): a row read (one chunk of 16 rows) and a transposing read (two chunks of 16
-// rows) both spread over the banks. Staging is single-buffered with the next step's global loads
-// issued into registers before the current step's matrix work.
+// rows) both spread over the banks. Tiles arrive by 16-byte direct-to-LDS loads from the BF16
+// copies (single-buffered; two workgroups per CU overlap one's loads with the other's work), and
+// fragment reads are issued in groups ahead of the matrix instructions that use them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
