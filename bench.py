@@ -49,6 +49,7 @@ WORKLOAD_TEXT = {
     "varlen": "varlen: 8 sequences, lengths uniform in [128, 4096] (seed 0), 16 heads, head_dim 128, 0.1% x20 outliers",
     "pertensor": "pertensor: 2 x 16384 tokens, 24 heads, head_dim 128, per-tensor FP8 e4m3 (no descale)",
     "cross": "cross: queries 4096 tokens, keys/values 32768 tokens, 16 heads, head_dim 128, keys N(0, 0.25)",
+    "batch8": "batch8: 8 sequences x 2048 tokens, 16 heads, head_dim 128, noncausal MHA (the README's bundled shape)",
 }
 
 

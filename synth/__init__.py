@@ -111,6 +111,9 @@ def make_workload(name: str, seed: int = 0, scale_tokens: int = 1) -> Workload:
     elif name == "cross":
         lq, lk = [4096], [32768]
         heads = 16
+    elif name == "batch8":  # the LP-FA4 README's bundled benchmark shape: 8 x 2048 tokens, 16 heads
+        lq = lk = [2048] * 8
+        heads = 16
     else:
         raise ValueError(f"unknown workload {name!r}")
     if scale_tokens > 1:
