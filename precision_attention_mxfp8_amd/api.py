@@ -560,10 +560,23 @@ class BwdPlan:
         tq, h = q.payload.shape[0], q.payload.shape[1]
         tk = k.payload.shape[0]
         dev = q.payload.device
+        if tq != meta_q.total_tokens or tk != meta_k.total_tokens:
+            raise ValueError("token counts do not match the metadata")
+        rq, rk = meta_q.total_scale_rows, meta_k.total_scale_rows
+        u8 = torch.uint8
         for t, name, shape, dtype in ((out, "out", (tq, h, HEAD_DIM), torch.bfloat16),
                                       (dout, "dout", (tq, h, HEAD_DIM), torch.bfloat16),
-                                      (lse, "lse", (h, tq), torch.float32)):
+                                      (lse, "lse", (h, tq), torch.float32),
+                                      (k.payload, "k", (tk, h, HEAD_DIM), u8), (v.payload, "v", (tk, h, HEAD_DIM), u8),
+                                      (q_t.payload, "q_t", (tq, h, HEAD_DIM), u8),
+                                      (k_t.payload, "k_t", (tk, h, HEAD_DIM), u8),
+                                      (q.scales, "q scales", (rq, h, 4), u8), (k.scales, "k scales", (rk, h, 4), u8),
+                                      (v.scales, "v scales", (rk, h, 4), u8),
+                                      (q_t.scales, "q_t scales", (rq // 32, h, HEAD_DIM), u8),
+                                      (k_t.scales, "k_t scales", (rk // 32, h, HEAD_DIM), u8)):
             _check_out(t, shape, dtype, dev, name)
+        if q.payload.dtype != u8:
+            raise ValueError("q must hold E4M3 codes (uint8)")
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
         self._keep = (q, k, v, q_t, k_t, out, dout, lse)

@@ -199,3 +199,17 @@ def test_cross_scaled():
     wl = make_workload("cross", seed=0, scale_tokens=8)
     case = Case(wl, seed=811, sel=[0, 15])
     _check_all(case, case.run())
+
+
+def test_mismatched_operands_are_rejected_before_launch():
+    wl = make_custom([40, 70], [50, 90], heads=2, seed=812)
+    case = Case(wl, seed=813)
+    qd, kd, vd, qt, kt = case.ops
+    other = make_custom([40, 70], [50, 90], heads=3, seed=814)
+    k3 = lp.quantize_mxfp8_varlen(bf16_to_device(other.k_bits), lp.VarlenMeta.from_lengths(other.lengths_k))
+    with pytest.raises(ValueError):   # K with 3 heads against Q with 2
+        lp.lp_attn_varlen_bwd(qd, k3, vd, qt, kt, case.out, case.dout, case.lse)
+    with pytest.raises(ValueError):   # Q's token orientation in place of K's
+        lp.lp_attn_varlen_bwd(qd, kd, vd, qt, qt, case.out, case.dout, case.lse)
+    with pytest.raises(ValueError):   # LSE of the wrong shape
+        lp.lp_attn_varlen_bwd(qd, kd, vd, qt, kt, case.out, case.dout, case.lse[:, :10])
