@@ -1,7 +1,7 @@
 /*
- * lpfa.h - C ABI of the MXFP8 attention-forward library for AMD Instinct MI355X (gfx950).
+ * lpfa.h - C ABI of the MXFP8 attention library for AMD Instinct MI355X (gfx950).
  *
- * The library does two things, both on the GPU, both on a stream the caller owns:
+ * The library does these things, all on the GPU, all on a stream the caller owns:
  *   1. MXFP8 quantization of packed variable-length (tokens, heads, 128) tensors:
  *      E4M3 payloads plus one E8M0 scale per 32-element block along head_dim, each
  *      sequence with its own scale storage padded to a multiple of 128 tokens
@@ -15,10 +15,17 @@
  *      Optional per-tensor q/k/v descales; a missing descale is read as 1.0 with the
  *      same arithmetic, so a unit descale gives bit-identical output (vLLM PR
  *      "FA4: no FP8 descale for a unit per-tensor scale", sections "Claims" and
- *      "Validation").
+ *      "Validation"). Variants: V MXFP8 along tokens (the second hardware
+ *      orientation), and BF16 Q/K (the BF16 FlashAttention forward, for comparison).
+ *   3. The backward of that attention on MXFP8 operands in both orientations: dQ in
+ *      BF16, dK and dV in BF16 or MXFP8 (LP-FA4 README, same section).
+ *   4. Per-tensor current scaling to E4M3 (TensorRT-LLM PR "TE FP8 attention backend for
+ *      VisualGen", inference scaling fix), and the forward's three preparation passes
+ *      (quantize Q and K, cast V) in one launch.
  *
  * Conventions for every entry point
- *   - All tensor arguments are DEVICE pointers to memory the caller allocated; the
+ *   - All tensor arguments are DEVICE pointers to memory the caller allocated (two
+ *     entry points also take a caller-owned workspace); the
  *     library never allocates, frees or synchronises, and launches only on `stream`
  *     (a hipStream_t passed as void*; NULL means the default stream).
  *   - Strides are in elements. Element types: BF16 = raw uint16 bit patterns,
