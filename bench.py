@@ -19,6 +19,7 @@ MXFP8 along tokens, and quantizer_tokens_gbps that V quantizer, graph-replayed;
 attention_bf16_fa_tflops = the BF16 FlashAttention forward (BF16 Q, K, V) on the same shapes,
 back-to-back, and mxfp8_speedup_vs_bf16_fa = its time over the MXFP8 forward's back-to-back time;
 cast_current_gbps = per-tensor current scaling of V (amax, then the scaled cast), graph-replayed;
+prepare_qkv_gbps = the one-launch preparation (Q, K quantized and V cast), graph-replayed;
 attention_bwd_tflops / _us / _pct_bf16_peak = the MXFP8 backward with MXFP8 dK/dV output,
 back-to-back (2.5 x the forward's FLOPs; its matrix products run in BF16);
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload.
@@ -214,6 +215,11 @@ def main():
             # algorithmic bytes are those of one cast (3 B per element); the amax pass reads V again
             cur_ms = graph_ms_per_call(torch, lambda: lp.cast_e4m3_current(v, out=vx))
             state["cast_current_gbps"] = round(v.numel() * 3 / (cur_ms * 1e-3) / 1e9, 1)
+            # the one-launch preparation (Q and K quantized, V cast), graph-replayed: algorithmic
+            # bytes of both quantizers plus the cast, and K's group maxima
+            pms = graph_ms_per_call(torch, lambda: lp.prepare_qkv(q, k, v, mq, mk, out=(qx, kx, vx)))
+            pbytes = qbytes + v.numel() * 3 + (mk.total_scale_rows // 16) * h
+            state["prepare_qkv_gbps"] = round(pbytes / (pms * 1e-3) / 1e9, 1)
 
     # ---- pv bf16 variant of the same workload, for the record ----
     extra = {}
@@ -319,8 +325,9 @@ def main():
         "cast_e4m3_gbps": None if cast_gbps is None else round(cast_gbps, 1),
         "pct_fp8_peak": round(100 * achieved / FP8_PEAK_TFLOPS, 2),
     }
-    if "cast_current_gbps" in state:
-        extra["cast_current_gbps"] = state["cast_current_gbps"]
+    for key in ("cast_current_gbps", "prepare_qkv_gbps"):
+        if key in state:
+            extra[key] = state[key]
     line.update(extra)
     print(json.dumps(line), flush=True)
 
