@@ -13,7 +13,7 @@
 // Kernels (in stream order)
 //  * bwd_dequant_kernel: Qd, Qt, Kd, Vd and Kt dequantized once into BF16 copies in the caller's
 //    workspace (the main kernels re-read every tile once per 64-row block of the other side).
-//  * bwd_delta_kernel: D for every (head, query) into the caller's workspace; 16 lanes per row.
+//    The same launch computes D for every (head, query) into the workspace (16 lanes per row).
 //  * bwd_dkdv_kernel: one workgroup = (64 keys of one sequence, head), 4 waves x 16 keys. The
 //    keys' K and V fragments and the dK, dV accumulators stay in registers while the workgroup
 //    walks the sequence's queries 64 at a time. The epilogue writes BF16, or quantizes each
@@ -160,11 +160,38 @@ __device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
 // matrix instructions that use them follow (one wait for the group instead of one per read).
 __device__ __forceinline__ void group_end() { __builtin_amdgcn_sched_barrier(0); }
 
+// ---- D = rowsum(dO * O)
+
+__device__ __forceinline__ void delta_rows(const BwdParams& p, int64_t gid) {
+  const int64_t row = gid >> 4;  // token * H + head
+  const int sub = threadIdx.x & 15;
+  const bool in = row < p.total_q * p.num_heads;
+  float acc = 0.0f;
+  if (in) {
+    const uint4 o = *reinterpret_cast<const uint4*>(p.out + row * 128 + sub * 8);
+    const uint4 d = *reinterpret_cast<const uint4*>(p.dout + row * 128 + sub * 8);
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += bf16_lo(ow[i]) * bf16_lo(dw[i]) + bf16_hi(ow[i]) * bf16_hi(dw[i]);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+  if (in && sub == 0) {
+    const int64_t tok = row / p.num_heads;
+    const int head = (int)(row - tok * p.num_heads);
+    p.delta[(int64_t)head * p.total_q + tok] = acc;
+  }
+}
+
 // ---- pre-pass: each MX operand dequantized once into a BF16 copy (tokens, H, 128)
 // blockIdx.y selects the tensor: 0 Qd, 1 Qt, 2 Kd, 3 Vd, 4 Kt (t: token orientation). A thread
 // converts one 8-element chunk of a padded scale row; pad rows have no tokens and are skipped.
 __global__ __launch_bounds__(256) void bwd_dequant_kernel(BwdParams p) {
   const int job = blockIdx.y;
+  if (job == 5) {  // D = rowsum(dO * O): 16 lanes per (query, head) row; Q's padded rows >= its tokens
+    delta_rows(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    return;
+  }
   const bool isq = job < 2, tok_orient = job == 1 || job == 4;
   const uint8_t* pay = job == 0 ? p.q : job == 1 ? p.q_t : job == 2 ? p.k : job == 3 ? p.v : p.k_t;
   const uint8_t* sc = job == 0 ? p.q_scale : job == 1 ? p.q_t_scale : job == 2 ? p.k_scale : job == 3 ? p.v_scale : p.k_t_scale;
@@ -193,30 +220,6 @@ __global__ __launch_bounds__(256) void bwd_dequant_kernel(BwdParams p) {
     out = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
   *reinterpret_cast<uint4*>(dst + off) = out;
-}
-
-// ---- D = rowsum(dO * O)
-
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid >> 4;  // token * H + head
-  const int sub = threadIdx.x & 15;
-  const bool in = row < p.total_q * p.num_heads;
-  float acc = 0.0f;
-  if (in) {
-    const uint4 o = *reinterpret_cast<const uint4*>(p.out + row * 128 + sub * 8);
-    const uint4 d = *reinterpret_cast<const uint4*>(p.dout + row * 128 + sub * 8);
-    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc += bf16_lo(ow[i]) * bf16_lo(dw[i]) + bf16_hi(ow[i]) * bf16_hi(dw[i]);
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-  if (in && sub == 0) {
-    const int64_t tok = row / p.num_heads;
-    const int head = (int)(row - tok * p.num_heads);
-    p.delta[(int64_t)head * p.total_q + tok] = acc;
-  }
 }
 
 // ---- epilogue: a 64 x 128 FP32 tile in LDS -> BF16 rows, or MXFP8 rows plus scale rows
@@ -522,13 +525,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 }  // namespace
 
 hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s) {
+  // the five operand copies and D in one launch (grid y = job); nothing to contract without
+  // both queries and keys (then the main kernels write zeros and read neither)
   const int64_t jobs_rows = p.rows_q > p.rows_k ? p.rows_q : p.rows_k;
   if (p.rows_q > 0 && p.rows_k > 0)
-    hipLaunchKernelGGL(bwd_dequant_kernel, dim3((unsigned)((jobs_rows * p.num_heads * 16 + 255) / 256), 5), dim3(256), 0,
+    hipLaunchKernelGGL(bwd_dequant_kernel, dim3((unsigned)((jobs_rows * p.num_heads * 16 + 255) / 256), 6), dim3(256), 0,
                        s, p);
-  const int64_t rows = p.total_q * p.num_heads;
-  if (rows > 0)
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, p);
   if (p.rows_k > 0)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.rows_k / BR), (unsigned)p.num_heads), dim3(256), 0, s, p);
   if (p.rows_q > 0)
