@@ -21,6 +21,21 @@ def test_hand_case():
     assert list(codes) == [0x71, 0xFE, 0x69]
 
 
+def test_quotient_rounded_to_float32_before_the_code():
+    """The codes are decided on the float32 quotient: amax 13 gives s = fl32(13/448), and the exact
+    quotient -9.75 / s lies within half a float32 spacing (2^-16 at 336) of -336, so fl32(-9.75 / s)
+    is -336 exactly, the midpoint of the E4M3 codes 320 (0x7A, even mantissa) and 352 (0x7B): the
+    tie goes to 0xFA. Multiplying by the float32 reciprocal of s instead lands one float32 step
+    past 336 and would give 0xFB."""
+    from fractions import Fraction
+    codes, s = current_quantize(np.array([13.0, -9.75], dtype=np.float32))
+    assert s == np.float32(13.0) / np.float32(448.0)
+    q = Fraction(-9.75) / Fraction(float(s))
+    assert abs(q + 336) < Fraction(1, 2 ** 16)
+    assert list(codes) == [0x7E, 0xFA]
+    assert np.float32(np.float32(-9.75) * (np.float32(1.0) / s)) != np.float32(-336.0)
+
+
 @pytest.mark.parametrize("k", [-20, -3, 0, 5, 30])
 def test_power_of_two_maximum_closed_form(k):
     """amax = 448 * 2^k gives s = 2^k exactly, so the codes are E4M3(x * 2^-k)."""

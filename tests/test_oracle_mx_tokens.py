@@ -74,6 +74,18 @@ def test_layout_padding_and_sequence_independence():
         assert np.array_equal(si[:nblk], scales[r0:r0 + nblk])
 
 
+def test_last_block_ignores_the_next_sequence():
+    """A sequence's last, partial 32-token block takes its maximum over its own tokens only: the
+    next sequence (here 2^10 times larger) changes neither its scales nor its codes."""
+    lengths = [45, 40]
+    wl = make_custom(lengths, lengths, heads=2, seed=22)
+    x = bf16_bits_to_f32(wl.q_bits).astype(np.float64)
+    x[45:] *= 2.0 ** 10
+    payload, scales, _ = mx_quantize_varlen_tokens(x, np.array([0, 45, 85]), "rceil")
+    p0, s0, _ = mx_quantize_varlen_tokens(x[:45], np.array([0, 45]), "rceil")
+    assert np.array_equal(scales[:2], s0[:2]) and np.array_equal(payload[:45], p0)
+
+
 @pytest.mark.parametrize("mode", ["rceil", "floor"])
 def test_dequant_error_bound(mode):
     """A round-to-nearest E4M3 code is within half its spacing; below the block maximum that is at most
