@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers to memory the caller allocated (two
- *     entry points also take a caller-owned workspace); the
+ *     entry points also take a caller-owned workspace; lp_fp8_cast_current_noalloc keeps
+ *     its scratch in a static device array instead); the
  *     library never allocates, frees or synchronises, and launches only on `stream`
  *     (a hipStream_t passed as void*; NULL means the default stream).
  *   - Strides are in elements. Element types: BF16 = raw uint16 bit patterns,
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 6
+#define LPFA_ABI_VERSION 7
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -188,6 +189,25 @@ int mxfp8_prepare_qkv(const void* q, const void* k, const void* v, int x_dtype, 
 int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                         int64_t total_tokens, int32_t num_heads, int32_t head_dim, float* work, uint8_t* y,
                         float* descale, void* stream);
+
+/* Floats in lp_fp8_cast_current's workspace: amax, then one partial maximum per amax workgroup. */
+#define LPFA_CURRENT_WORK_FLOATS 257
+
+/*
+ * lp_fp8_cast_current_noalloc - lp_fp8_cast_current without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and errors as lp_fp8_cast_current
+ * minus `work`: the partial maxima live in a static device array of the library (2 KB per GPU,
+ * held until the process ends), which holds what every input size needs, so no size is rejected
+ * for it. The call allocates nothing and needs no clearing (each call writes every partial
+ * maximum it reads). All calls on one GPU share that array: calls that overlap on one GPU
+ * (concurrent streams, or several threads) race and must be serialised by the caller.
+ * Errors: those of lp_fp8_cast_current; LPFA_EIO if the array's device address cannot be
+ * obtained.
+ */
+int lp_fp8_cast_current_noalloc(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                                int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
+                                float* descale, void* stream);
 
 /*
  * Arguments of lp_attn_varlen_fwd. Zero-initialise, then set struct_size =

@@ -20,10 +20,11 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
 PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
-           "mxfp8_prepare_qkv", "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_attn_varlen_fwd", "lp_attn_varlen_bwd")
+           "mxfp8_prepare_qkv", "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_fp8_cast_current_noalloc", "lp_attn_varlen_fwd",
+           "lp_attn_varlen_bwd")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -127,6 +128,8 @@ def load() -> ctypes.CDLL:
         lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p]
         lib.lp_fp8_cast_current.restype = ctypes.c_int
         lib.lp_fp8_cast_current.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p]
+        lib.lp_fp8_cast_current_noalloc.restype = ctypes.c_int
+        lib.lp_fp8_cast_current_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p]
         lib.lp_attn_varlen_fwd.restype = ctypes.c_int
         lib.lp_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnArgs), _p]
         lib.lp_attn_varlen_bwd.restype = ctypes.c_int

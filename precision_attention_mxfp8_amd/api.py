@@ -285,6 +285,23 @@ def cast_e4m3_current(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> Tu
     return out, descale
 
 
+def cast_e4m3_current_noalloc(x: torch.Tensor, out: torch.Tensor, descale: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """:func:`cast_e4m3_current` for callers that cannot allocate (HIP graph capture, serving loops):
+    ``out`` (uint8, x's shape, contiguous) and ``descale`` (one float32 element) are given, and the
+    library keeps its scratch in a static device array, so nothing is allocated. Calls that
+    overlap on one GPU share that array and must be serialised."""
+    dt = _fp_input(x)
+    t, h, _ = x.shape
+    _check_out(out, (t, h, HEAD_DIM), torch.uint8, x.device, "out")
+    if descale.dtype != torch.float32 or descale.numel() != 1 or descale.device != x.device:
+        raise ValueError("descale must be a one-element float32 tensor on x's device")
+    rc = _lib.load().lp_fp8_cast_current_noalloc(x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM,
+                                                 out.data_ptr(), descale.data_ptr(), _stream())
+    if rc:
+        _lib.check("lp_fp8_cast_current_noalloc", rc)
+    return out, descale
+
+
 def _as_codes(t: torch.Tensor) -> torch.Tensor:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8)

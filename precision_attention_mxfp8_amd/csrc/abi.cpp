@@ -167,6 +167,38 @@ int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t 
   return launch_status(lpfa::launch_cast_current(p, static_cast<hipStream_t>(stream)), "current-scaled cast");
 }
 
+int lp_fp8_cast_current_noalloc(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
+                                int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
+                                float* descale, void* stream) {
+  if (int rc = lpfa::check_cast(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads, head_dim, y))
+    return rc;
+  if (descale == nullptr || (reinterpret_cast<uintptr_t>(descale) & 3u)) {
+    lpfa::set_error("descale is NULL or not 4-byte aligned");
+    return LPFA_EINVAL;
+  }
+  float* ws = nullptr;
+  int capacity = 0;
+  if (hipError_t e = lpfa::current_scratch(&ws, &capacity); e != hipSuccess) {
+    lpfa::set_error(std::string("static scratch address: ") + hipGetErrorString(e));
+    return LPFA_EIO;
+  }
+  if (capacity < LPFA_CURRENT_WORK_FLOATS) {  // the partial maxima of any input size fit
+    lpfa::set_error("static scratch smaller than the current-scaling workspace");
+    return LPFA_EINVAL;
+  }
+  lpfa::CastParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.total_tokens = total_tokens;
+  p.num_heads = num_heads;
+  p.y = y;
+  p.amax = ws;
+  p.descale = descale;
+  return launch_status(lpfa::launch_cast_current(p, static_cast<hipStream_t>(stream)), "current-scaled cast");
+}
+
 int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   if (int rc = lpfa::check_attn(a)) return rc;
   lpfa::AttnParams p{};

@@ -112,6 +112,8 @@ hipError_t launch_cast(const CastParams& p, hipStream_t s);
 hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, const CastParams& pv,
                               hipStream_t s);  // quantize Q, K and cast V in one launch (one dtype)
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s);  // amax, then E4M3(x / s)
+// device address and size (floats) of the static scratch for current scaling on the current device
+hipError_t current_scratch(float** out, int* capacity);
 hipError_t launch_attention(const AttnParams& p, bool mx, int pv_mode, hipStream_t s,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s);  // D, then dK/dV, then dQ

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -310,7 +312,38 @@ __global__ __launch_bounds__(256) void cast_current_kernel(CastParams p) {
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
 }
 
+// Scratch of the allocation-free current-scaling entry point: the partial maxima that
+// amax_kernel hands to cast_current_kernel, in a file-scope device array instead of a caller
+// workspace. Every GPU the library runs on holds its own copy (2 KB) until the process ends.
+// Each call's amax_kernel writes all the partial maxima its cast_current_kernel reads, so nothing
+// needs clearing; calls that overlap on one GPU share the array and race.
+constexpr int CURRENT_SCRATCH_FLOATS = 512;
+static_assert(CURRENT_SCRATCH_FLOATS >= 1 + AMAX_BLOCKS && LPFA_CURRENT_WORK_FLOATS == 1 + AMAX_BLOCKS,
+              "scratch holds amax and every partial maximum");
+static __device__ __align__(256) float scratch[CURRENT_SCRATCH_FLOATS];
+
 }  // namespace
+
+// The scratch array's device address on the current device. The name `scratch` in host code is a
+// host-side stand-in, not a device address, so the address is looked up once per device and kept.
+hipError_t current_scratch(float** out, int* capacity) {
+  static std::mutex mu;
+  static float* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = static_cast<float*>(ptr);
+  }
+  *out = ptrs[dev];
+  *capacity = CURRENT_SCRATCH_FLOATS;
+  return hipSuccess;
+}
 
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s) {
   const int64_t chunks = p.total_tokens * p.num_heads * 16;

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 6
+    assert lib.lpfa_abi_version() == 7
 
 
 @pytest.mark.parametrize("cname,pystruct", [("lpfa_attn_args", _lib.AttnArgs), ("lpfa_bwd_args", _lib.BwdArgs)])
