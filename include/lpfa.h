@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 7
+#define LPFA_ABI_VERSION 8
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -136,7 +136,7 @@ int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok,
                                  uint8_t* scales, void* stream);
 
 /*
- * lp_fp8_cast_e4m3 - unscaled E4M3 cast (the fp8 PV mode's V).
+ * lp_fp8_cast_e4m3 - unscaled E4M3 cast (the fp8 PV mode's V; per-tensor FP8 Q, K, V).
  * (FastVideo PR "fp8 PV mode for the FA4-FP4 attention path": an elementwise e4m3 cast
  *  of V with no scale factors; the attention reads it with dequant scale 1.0.)
  *
@@ -145,10 +145,15 @@ int mxfp8_quantize_varlen_tokens(const void* x, int x_dtype, int64_t stride_tok,
  *   underflow give 0x80).
  *   x: BF16 or FP32, 16-byte aligned with 16-byte-multiple strides; y: uint8
  *   (total_tokens, num_heads, 128) contiguous. head_dim must be 128.
+ *   group_max: optional output (NULL: not written, ABI 8) uint8 (ceil(total_tokens / 16),
+ *   num_heads): entry [g, h] is the largest code magnitude (code & 0x7F) of head h over tokens
+ *   16g .. 16g+15 (those that exist). Passed to lp_attn_varlen_fwd as k_scale_group_max for a
+ *   per-tensor K, it gives the precision guard its bound on |k| (vLLM unit-descale PR: per-tensor
+ *   FP8 attention; without it the guard must assume the E4M3 range, 448).
  */
 int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                      int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
-                     void* stream);
+                     uint8_t* group_max, void* stream);
 
 /*
  * mxfp8_prepare_qkv - the forward's three preparation passes in one launch: Q and K as
@@ -208,6 +213,9 @@ int lp_fp8_cast_current(const void* x, int x_dtype, int64_t stride_tok, int64_t 
 int lp_fp8_cast_current_noalloc(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                                 int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
                                 float* descale, void* stream);
+
+/* Default threshold of the attention's precision guard (lpfa_attn_args.fp8_score_guard). */
+#define LPFA_FP8_SCORE_GUARD_DEFAULT 16.0f
 
 /*
  * Arguments of lp_attn_varlen_fwd. Zero-initialise, then set struct_size =
@@ -282,11 +290,15 @@ typedef struct lpfa_attn_args {
   void* start_event;
   void* stop_event;
 
-  /* Optional (MX mode): the group_max output of mxfp8_quantize_varlen for K, uint8
-   * (cu_scale_k[num_seqs] / 16, num_heads). When set, the precision guard (which picks
-   * the FP8 or the BF16 score path of a query tile, from bounds on |q| and |k|) reads the
-   * K bound there instead of scanning k_scale; the guard's decisions, and so the
-   * results, are the same either way. Ignored in per-tensor mode. */
+  /* Optional K maxima for the precision guard (which picks the FP8 or the BF16 score path of a
+   * query tile, from bounds on |q| and |k|; see fp8_score_guard).
+   * MX mode: the group_max output of mxfp8_quantize_varlen for K, uint8
+   * (cu_scale_k[num_seqs] / 16, num_heads); the guard reads the K bound there instead of
+   * scanning k_scale, and its decisions, and so the results, are the same either way.
+   * Per-tensor mode (ABI 8): the group_max output of lp_fp8_cast_e4m3 for K, uint8
+   * (ceil(total_k / 16), num_heads), per 16 packed tokens; the guard bounds |k| by the largest
+   * code of the groups that hold a sequence's keys (instead of 448, which sends typical data
+   * to the BF16 score path). Ignored with qk_bf16. */
   const uint8_t* k_scale_group_max;
 
   /* LPFA_PV_MX only (required there, else must be NULL): V's token-block scales from
@@ -299,6 +311,16 @@ typedef struct lpfa_attn_args {
    * bytes), scores are BF16 products summed in FP32, and pv_mode must be LPFA_PV_BF16; q_scale
    * and k_scale must be NULL (q/k descales still apply). 0: E4M3 q and k as above. */
   int32_t qk_bf16;
+
+  /* Threshold of the precision guard (ABI 8). A query tile computes its scores with the FP8
+   * matrix instruction when c * max|q| * max|k| <= fp8_score_guard, with c = softmax_scale *
+   * log2(e) * qd * kd and the bounds taken from the block scales (MX mode) or the codes and
+   * k_scale_group_max (per-tensor mode); otherwise with BF16 products of the exactly
+   * dequantized operands. The FP8 instruction truncates each product toward zero onto a grid 13
+   * bits below the largest exponent sum of its group of 8, so FP8 scores err by at most about
+   * 0.0137 * fp8_score_guard in log2 units (random-sign data by far less). 0 selects
+   * LPFA_FP8_SCORE_GUARD_DEFAULT; a negative value never takes FP8 scores; NaN is LPFA_EINVAL. */
+  float fp8_score_guard;
 } lpfa_attn_args;
 
 /*

@@ -11,13 +11,13 @@ Public API (marshalling only; the work runs in liblpfa.so):
 """
 from .api import (AttnPlan, BwdPlan, Mxfp8Tensor, Mxfp8TokensTensor, VarlenMeta, cast_e4m3, cast_e4m3_current,
                   cast_e4m3_current_noalloc,
-                  longest_first_tile_order,
+                  e4m3_group_max_shape, longest_first_tile_order,
                   lp_attn_varlen_bwd, lp_attn_varlen_fwd, prepare_qkv, quantize_mxfp8_varlen,
                   quantize_mxfp8_varlen_tokens)
 from ._lib import LpfaError, load as load_library
 
 __all__ = ["AttnPlan", "BwdPlan", "Mxfp8Tensor", "Mxfp8TokensTensor", "VarlenMeta", "cast_e4m3", "cast_e4m3_current",
            "cast_e4m3_current_noalloc",
-           "longest_first_tile_order",
+           "e4m3_group_max_shape", "longest_first_tile_order",
            "lp_attn_varlen_bwd", "lp_attn_varlen_fwd", "prepare_qkv", "quantize_mxfp8_varlen", "quantize_mxfp8_varlen_tokens", "LpfaError",
            "load_library"]

@@ -20,7 +20,7 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
 PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
            "mxfp8_prepare_qkv", "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_fp8_cast_current_noalloc", "lp_attn_varlen_fwd",
@@ -60,6 +60,7 @@ class AttnArgs(ctypes.Structure):
         ("k_scale_group_max", _p),
         ("v_scale", _p),
         ("qk_bf16", _i32),
+        ("fp8_score_guard", ctypes.c_float),
     ]
 
 
@@ -125,7 +126,7 @@ def load() -> ctypes.CDLL:
                                           _p, _p, _p, _p, _i32, _i64, _i64, ctypes.c_int,
                                           _p, _p, _p, _p, _p, _p, _p]
         lib.lp_fp8_cast_e4m3.restype = ctypes.c_int
-        lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p]
+        lib.lp_fp8_cast_e4m3.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p]
         lib.lp_fp8_cast_current.restype = ctypes.c_int
         lib.lp_fp8_cast_current.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p]
         lib.lp_fp8_cast_current_noalloc.restype = ctypes.c_int

@@ -248,18 +248,30 @@ def prepare_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta_q: Varle
     return qo, ko, vo
 
 
-def cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Unscaled E4M3 cast (fp8 PV mode's V): uint8 codes, same (tokens, heads, 128) shape, contiguous.
+def e4m3_group_max_shape(tokens: int, heads: int) -> Tuple[int, int]:
+    """Shape of :func:`cast_e4m3`'s group maxima: one byte per 16 tokens and head."""
+    return (-(-int(tokens) // 16), int(heads))
 
-    ``out``: a contiguous uint8 tensor of that shape to write into; a new one otherwise."""
+
+def cast_e4m3(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+              group_max_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unscaled E4M3 cast (fp8 PV mode's V; per-tensor FP8 Q, K, V): uint8 codes, same
+    (tokens, heads, 128) shape, contiguous.
+
+    ``out``: a contiguous uint8 tensor of that shape to write into; a new one otherwise.
+    ``group_max_out``: optional contiguous uint8 tensor of :func:`e4m3_group_max_shape` that
+    receives the largest code magnitude of every 16 tokens of each head; for a per-tensor K, pass
+    it to :func:`lp_attn_varlen_fwd` as ``k_group_max`` (the precision guard's bound on |k|)."""
     dt = _fp_input(x)
     t, h, _ = x.shape
     if out is None:
         out = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
     else:
         _check_out(out, (t, h, HEAD_DIM), torch.uint8, x.device, "out")
+    if group_max_out is not None:
+        _check_out(group_max_out, e4m3_group_max_shape(t, h), torch.uint8, x.device, "group_max_out")
     rc = _lib.load().lp_fp8_cast_e4m3(x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM,
-                                      out.data_ptr(), _stream())
+                                      out.data_ptr(), _ptr(group_max_out), _stream())
     if rc:
         _lib.check("lp_fp8_cast_e4m3", rc)
     return out
@@ -359,7 +371,8 @@ class AttnPlan:
                  mx: bool = True, softmax_scale: Optional[float] = None, q_descale: Descale = None,
                  k_descale: Descale = None, v_descale: Descale = None,
                  tile_order: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 lse: Optional[torch.Tensor] = None, qk_bf16: bool = False):
+                 lse: Optional[torch.Tensor] = None, qk_bf16: bool = False,
+                 fp8_score_guard: Optional[float] = None):
         if qk_bf16 and (mx or pv_mode != "bf16"):
             raise ValueError("BF16 q/k (qk_bf16) need mx=False and pv_mode='bf16'")
         if pv_mode not in _lib.PV_MODES:
@@ -405,6 +418,10 @@ class AttnPlan:
         a.num_heads, a.head_dim = h, HEAD_DIM
         a.softmax_scale = float(softmax_scale)
         a.causal = 0
+        if fp8_score_guard is not None:
+            if not float(fp8_score_guard) != 0.0 or math.isnan(float(fp8_score_guard)):
+                raise ValueError("fp8_score_guard must be a non-zero number (negative: never FP8 scores)")
+            a.fp8_score_guard = float(fp8_score_guard)
         a.q_descale, a.k_descale, a.v_descale = _ptr(qd), _ptr(kd), _ptr(vd)
         a.q_descale_stride_seq, a.q_descale_stride_head = qss, qsh
         a.k_descale_stride_seq, a.k_descale_stride_head = kss, ksh
@@ -434,13 +451,16 @@ class AttnPlan:
                              f"along head_dim (got {t.dtype} {tuple(t.shape)} on {t.device})")
 
     def __call__(self, q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor, torch.Tensor],
-                 v: torch.Tensor, timing: Optional[Tuple] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 v: torch.Tensor, timing: Optional[Tuple] = None,
+                 k_group_max: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
         a = self._args
         if self.mx:
             if not (isinstance(q, Mxfp8Tensor) and isinstance(k, Mxfp8Tensor)):
                 raise ValueError("this plan is block-scaled: q and k must be Mxfp8Tensor")
-            if (q.meta is not self.meta_q and q.meta.cu_scale_host != self.meta_q.cu_scale_host) or \
-                    (k.meta is not self.meta_k and k.meta.cu_scale_host != self.meta_k.cu_scale_host):
+            if k_group_max is not None:
+                raise ValueError("k_group_max is for per-tensor K; an Mxfp8Tensor K carries its own group_max")
+            if (q.meta is not self.meta_q and q.meta.lengths != self.meta_q.lengths) or \
+                    (k.meta is not self.meta_k and k.meta.lengths != self.meta_k.lengths):
                 raise ValueError("q/k were quantized with different sequence metadata")
             qp, kp = q.payload, k.payload
             a.q_scale, a.k_scale = q.scales.data_ptr(), k.scales.data_ptr()
@@ -451,19 +471,26 @@ class AttnPlan:
                 a.k_scale_group_max = gm.data_ptr()
             else:
                 a.k_scale_group_max = None
-            if q.scales.shape != (self.meta_q.total_scale_rows, self.num_heads, 4) or \
-                    k.scales.shape != (self.meta_k.total_scale_rows, self.num_heads, 4):
-                raise ValueError("scale tensors do not match the metadata")
+            _check_out(q.scales, (self.meta_q.total_scale_rows, self.num_heads, 4), torch.uint8, self._dev, "q.scales")
+            _check_out(k.scales, (self.meta_k.total_scale_rows, self.num_heads, 4), torch.uint8, self._dev, "k.scales")
         else:
             if isinstance(q, Mxfp8Tensor) or isinstance(k, Mxfp8Tensor):
                 raise ValueError("this plan takes raw q and k (E4M3 codes, or BF16 with qk_bf16)")
             qp, kp = q, k
+            if k_group_max is not None:
+                if self.qk_bf16:
+                    raise ValueError("k_group_max is for E4M3 K")
+                _check_out(k_group_max, e4m3_group_max_shape(self.meta_k.total_tokens, self.num_heads), torch.uint8,
+                           self._dev, "k_group_max")
+                a.k_scale_group_max = k_group_max.data_ptr()
+            else:
+                a.k_scale_group_max = None
         self._operand(qp, self._qshape, self._qkdtype, "q")
         self._operand(kp, self._kshape, self._qkdtype, "k")
         if self.pv_mode == "mx":
             if not isinstance(v, Mxfp8TokensTensor):
                 raise ValueError("pv_mode='mx' needs v as an Mxfp8TokensTensor (quantize_mxfp8_varlen_tokens)")
-            if v.meta is not self.meta_k and v.meta.cu_scale_host != self.meta_k.cu_scale_host:
+            if v.meta is not self.meta_k and v.meta.lengths != self.meta_k.lengths:
                 raise ValueError("v was quantized with different sequence metadata")
             vs, sshape = v.scales, (self.meta_k.total_scale_rows // 32, self.num_heads, HEAD_DIM)
             if vs.shape != sshape or vs.dtype != torch.uint8 or not vs.is_contiguous() or vs.device != self._dev:
@@ -499,7 +526,9 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
                        tile_order: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None,
                        lse: Optional[torch.Tensor] = None,
-                       timing: Optional[Tuple] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       timing: Optional[Tuple] = None,
+                       k_group_max: Optional[torch.Tensor] = None,
+                       fp8_score_guard: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Noncausal head_dim-128 attention forward over packed sequences -> (out BF16 (Tq,H,128), lse FP32 (H,Tq)).
 
     ``q``/``k`` are Mxfp8Tensor (block-scaled QK^T), raw E4M3 codes (per-tensor FP8 mode), or
@@ -509,6 +538,9 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
     ``timing``: optional (start, stop) ``torch.cuda.Event`` pair with timing enabled, each
     recorded once before (so the handles exist); the kernel's dispatch stamps them, and
     ``start.elapsed_time(stop)`` is then the kernel's own duration.
+    ``k_group_max``: per-tensor mode, the group maxima of K's cast (:func:`cast_e4m3`), which give
+    the precision guard its bound on |k|. ``fp8_score_guard``: the guard's threshold (default 16;
+    negative: never FP8 scores).
     """
     if pv_mode not in _lib.PV_MODES:
         raise ValueError(f"pv_mode must be one of {sorted(_lib.PV_MODES)}, got {pv_mode!r}")
@@ -541,8 +573,9 @@ def lp_attn_varlen_fwd(q: Union[Mxfp8Tensor, torch.Tensor], k: Union[Mxfp8Tensor
         raise ValueError("q, k and v must have the same number of heads")
     plan = AttnPlan(meta_q, meta_k, h, pv_mode=pv_mode, mx=mx_q, softmax_scale=softmax_scale,
                     q_descale=q_descale, k_descale=k_descale, v_descale=v_descale, tile_order=tile_order,
-                    out=out, lse=lse, qk_bf16=qk_bf16)
-    return plan(q if mx_q else qp, k if mx_k else kp, vt if pv_mode == "mx" else v, timing=timing)
+                    out=out, lse=lse, qk_bf16=qk_bf16, fp8_score_guard=fp8_score_guard)
+    return plan(q if mx_q else qp, k if mx_k else kp, vt if pv_mode == "mx" else v, timing=timing,
+                k_group_max=k_group_max)
 
 
 class BwdPlan:

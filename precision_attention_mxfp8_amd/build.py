@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["quant.hip", "attn_fwd.hip", "attn_bwd.hip", "abi.cpp", "validate.cpp"]
 OUTPUT = os.path.join(PKG, "liblpfa.so")
+# measured-ceiling microbenchmarks for the benchmark's roofline fractions (not part of the C ABI)
+PEAK_SOURCE = "peak.hip"
+PEAK_OUTPUT = os.path.join(PKG, "libpeak.so")
 
 
 def hipcc() -> str:
@@ -17,7 +20,8 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build_command(output: str = OUTPUT):
+def build_command(output: str = OUTPUT, sources=None):
+    sources = SOURCES if sources is None else sources
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed FP32 VALU ops stay off: scalar float code only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,13 +36,12 @@ def build_command(output: str = OUTPUT):
             # once and spills the two-group loop
             "-mllvm", "-disable-machine-sink",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", output] + \
-           [os.path.join(CSRC, s) for s in SOURCES]
+           [os.path.join(CSRC, s) for s in sources]
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source into liblpfa.so (always recompiles). Returns the library path."""
-    tmp = OUTPUT + ".tmp"
-    cmd = build_command(tmp)
+def _compile(output: str, sources, verbose: bool) -> None:
+    tmp = output + ".tmp"
+    cmd = build_command(tmp, sources)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
@@ -46,7 +49,14 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, OUTPUT)
+    os.replace(tmp, output)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source into liblpfa.so, and the ceiling microbenchmarks into libpeak.so
+    (always recompiles). Returns the product library's path."""
+    _compile(OUTPUT, SOURCES, verbose)
+    _compile(PEAK_OUTPUT, [PEAK_SOURCE], verbose)
     return OUTPUT
 
 

@@ -127,7 +127,7 @@ int mxfp8_prepare_qkv(const void* q, const void* k, const void* v, int x_dtype, 
 
 int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_head,
                      int64_t total_tokens, int32_t num_heads, int32_t head_dim, uint8_t* y,
-                     void* stream) {
+                     uint8_t* group_max, void* stream) {
   if (int rc = lpfa::check_cast(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads, head_dim, y))
     return rc;
   lpfa::CastParams p{};
@@ -138,6 +138,7 @@ int lp_fp8_cast_e4m3(const void* x, int x_dtype, int64_t stride_tok, int64_t str
   p.total_tokens = total_tokens;
   p.num_heads = num_heads;
   p.y = y;
+  p.group_max = group_max;
   return launch_status(lpfa::launch_cast(p, static_cast<hipStream_t>(stream)), "e4m3 cast");
 }
 
@@ -236,9 +237,10 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
     const int64_t kspan = a->total_k > 0 ? ((a->total_k - 1) * a->k_stride_tok + (int64_t)(a->num_heads - 1) * a->k_stride_head + 128) * kb : 0;
     const int64_t vspan = a->total_k > 0 ? ((a->total_k - 1) * a->v_stride_tok + (int64_t)(a->num_heads - 1) * a->v_stride_head + 128) * vb : 0;
     p.k_end = a->k + kspan;
-    p.k_gmax = a->q_scale != nullptr ? a->k_scale_group_max : nullptr;
+    p.k_gmax = a->qk_bf16 ? nullptr : a->k_scale_group_max;  // MX scale maxima or per-tensor code maxima
     p.v_scale = a->v_scale;
     p.qk_bf16 = a->qk_bf16;
+    p.guard = a->fp8_score_guard == 0.0f ? LPFA_FP8_SCORE_GUARD_DEFAULT : a->fp8_score_guard;
     p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
   }
   p.total_q = a->total_q;

@@ -31,6 +31,7 @@ struct CastParams {
   uint8_t* y;
   float* amax;     // current scaling: amax[0] = the tensor's largest magnitude; amax[1..256]: partial maxima
   float* descale;  // current scaling: s = amax / 448 (1 for an all-zero tensor)
+  uint8_t* group_max;  // unscaled cast, optional: largest code magnitude of each (16 tokens, head)
 };
 
 struct AttnParams {
@@ -49,7 +50,7 @@ struct AttnParams {
   const int32_t* tile_order;
   uint16_t* out;
   float* lse;
-  const uint8_t* k_gmax;   // optional per-(16-row scale group, head) maximum K scale byte
+  const uint8_t* k_gmax;   // optional K maxima per (16 rows, head): MX scale bytes / per-tensor code magnitudes
   const uint8_t* v_scale;  // V's token-block scales (MX V only)
   const uint8_t* k_end;    // one past the last byte of K / V: loads beyond read zeros
   const uint8_t* v_end;
@@ -62,6 +63,7 @@ struct AttnParams {
   int32_t num_tiles;  // work tiles to run
   float scale_log2;   // softmax_scale * log2(e)
   int32_t qk_bf16;    // Q and K are BF16 (the BF16 FlashAttention forward)
+  float guard;        // FP8 scores when c * max|q| * max|k| <= guard (negative: never)
 };
 
 // Attention backward (lp_attn_varlen_bwd); every tensor contiguous, (tokens, heads, 128).

@@ -221,9 +221,47 @@ __device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
 }
 
+// The cast with group maxima (per-tensor K for the attention's precision guard): a workgroup
+// owns 16 consecutive tokens of one head (bid enumerates (16-token group, head), heads fastest),
+// 16 lanes per token as in cast_block, and writes the largest code magnitude of its 2048 codes
+// (codes order like magnitudes, and the RNE conversion is monotonic, so that is the code of
+// the largest clamped magnitude). Tokens past the end are not read and count as zero.
+template <typename T>
+__device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid, float* red) {
+  const int h = (int)(bid % (unsigned)p.num_heads);
+  const int64_t t = (int64_t)(bid / (unsigned)p.num_heads) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float m = 0.0f;
+  if (t < p.total_tokens) {
+    float v[8];
+    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = clamp448(v[i]);
+      m = fmaxf(m, fabsf(v[i]));
+    }
+    const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<uint2*>(p.y + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float g = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    p.group_max[(int64_t)(bid / (unsigned)p.num_heads) * p.num_heads + h] = (uint8_t)(cvt_pk_e4m3(g, 0.0f) & 0x7Fu);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
   cast_block<T>(p, blockIdx.x);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void e4m3_cast_gmax_kernel(CastParams p) {
+  __shared__ float red[4];
+  cast_group<T>(p, blockIdx.x, red);
 }
 
 // The three preparation passes of a forward in one launch: Q's and K's MXFP8 quantization and
@@ -396,6 +434,14 @@ hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, cons
 hipError_t launch_cast(const CastParams& p, hipStream_t s) {
   const int64_t threads = p.total_tokens * p.num_heads * 16;
   if (threads == 0) return hipSuccess;
+  if (p.group_max != nullptr) {
+    const dim3 grid((unsigned)((p.total_tokens + 15) / 16 * p.num_heads));
+    if (p.x_dtype == LPFA_DTYPE_BF16)
+      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<float>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (p.x_dtype == LPFA_DTYPE_BF16)
     hipLaunchKernelGGL(e4m3_cast_kernel<uint16_t>, grid, dim3(256), 0, s, p);

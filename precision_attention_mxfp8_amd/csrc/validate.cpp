@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstring>
 #include <sstream>
 
 namespace lpfa {
@@ -102,6 +103,21 @@ int check_cast(const void* x, int x_dtype, int64_t stride_tok, int64_t stride_he
   return LPFA_OK;
 }
 
+// Float classification from the bits: the library is compiled with -fno-honor-nans (the kernels'
+// inputs are finite by contract), under which std::isnan / std::isfinite may fold to constants,
+// but host arguments still have to be checked for NaN and infinity.
+static bool float_is_nan(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, sizeof b);
+  return (b & 0x7FFFFFFFu) > 0x7F800000u;
+}
+
+static bool float_finite_positive(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, sizeof b);
+  return (b >> 31) == 0 && (b & 0x7F800000u) != 0x7F800000u && b != 0;
+}
+
 int check_attn(const lpfa_attn_args* a) {
   if (a == nullptr) return fail(LPFA_EINVAL, "args is NULL");
   if (a->struct_size < (int32_t)sizeof(lpfa_attn_args))
@@ -124,8 +140,9 @@ int check_attn(const lpfa_attn_args* a) {
   if (a->num_seqs < 0 || a->num_heads < 1 || a->total_q < 0 || a->total_k < 0 ||
       a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
     return fail(LPFA_EINVAL, "negative size, or num_heads < 1");
-  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale > 0.0f))
+  if (!float_finite_positive(a->softmax_scale))
     return fail(LPFA_EINVAL, "softmax_scale must be finite and positive");
+  if (float_is_nan(a->fp8_score_guard)) return fail(LPFA_EINVAL, "fp8_score_guard is NaN");
   if ((a->q_scale == nullptr) != (a->k_scale == nullptr))
     return fail(LPFA_EINVAL, "q_scale and k_scale must both be set (MX mode) or both be NULL (per-tensor mode)");
   if (a->q_scale && (a->cu_scale_q == nullptr || a->cu_scale_k == nullptr))
@@ -175,7 +192,7 @@ int check_bwd(const lpfa_bwd_args* a) {
     return fail(LPFA_EINVAL, "total scale rows must be multiples of 128");
   if (a->total_scale_rows_q < a->total_q || a->total_scale_rows_k < a->total_k)
     return fail(LPFA_EINVAL, "total scale rows below the token count");
-  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale > 0.0f))
+  if (!float_finite_positive(a->softmax_scale))
     return fail(LPFA_EINVAL, "softmax_scale must be finite and positive");
   if (a->output_mxfp8_dkv != 0 && a->output_mxfp8_dkv != 1) return fail(LPFA_EINVAL, "output_mxfp8_dkv must be 0 or 1");
   if (a->scaling_mode != LPFA_SCALING_RCEIL && a->scaling_mode != LPFA_SCALING_FLOOR)

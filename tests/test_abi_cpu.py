@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 7
+    assert lib.lpfa_abi_version() == 8
 
 
 @pytest.mark.parametrize("cname,pystruct", [("lpfa_attn_args", _lib.AttnArgs), ("lpfa_bwd_args", _lib.BwdArgs)])
@@ -156,10 +156,10 @@ def test_prepare_rejects(lib):
 
 
 def test_cast_rejects(lib):
-    assert lib.lp_fp8_cast_e4m3(FAKE, 0, 256, 128, 2, 2, 96, FAKE, None) == _lib.LPFA_ENOTSUP
-    assert lib.lp_fp8_cast_e4m3(FAKE, 2, 256, 128, 2, 2, 128, FAKE, None) == _lib.LPFA_EINVAL
-    assert lib.lp_fp8_cast_e4m3(FAKE, 0, 256, 128, 2, 2, 128, None, None) == _lib.LPFA_EINVAL
-    assert lib.lp_fp8_cast_e4m3(FAKE + 8, 0, 256, 128, 2, 2, 128, FAKE, None) == _lib.LPFA_EINVAL
+    assert lib.lp_fp8_cast_e4m3(FAKE, 0, 256, 128, 2, 2, 96, FAKE, None, None) == _lib.LPFA_ENOTSUP
+    assert lib.lp_fp8_cast_e4m3(FAKE, 2, 256, 128, 2, 2, 128, FAKE, None, None) == _lib.LPFA_EINVAL
+    assert lib.lp_fp8_cast_e4m3(FAKE, 0, 256, 128, 2, 2, 128, None, None, None) == _lib.LPFA_EINVAL
+    assert lib.lp_fp8_cast_e4m3(FAKE + 8, 0, 256, 128, 2, 2, 128, FAKE, None, None) == _lib.LPFA_EINVAL
 
 
 def _args(**kw):
@@ -201,6 +201,9 @@ def _args(**kw):
     (dict(v_descale=FAKE), _lib.LPFA_EINVAL),       # v descale with BF16 V
     (dict(softmax_scale=0.0), _lib.LPFA_EINVAL),
     (dict(softmax_scale=float("nan")), _lib.LPFA_EINVAL),
+    (dict(fp8_score_guard=float("nan")), _lib.LPFA_EINVAL),
+    (dict(softmax_scale=float("inf")), _lib.LPFA_EINVAL),
+    (dict(softmax_scale=-0.0), _lib.LPFA_EINVAL),
     (dict(q=None), _lib.LPFA_EINVAL),
     (dict(v=FAKE + 4), _lib.LPFA_EINVAL),
     (dict(k_stride_tok=100), _lib.LPFA_EINVAL),

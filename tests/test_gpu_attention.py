@@ -16,7 +16,8 @@ import torch
 import oracle
 import precision_attention_mxfp8_amd as lp
 from synth import make_workload, make_custom
-from helpers import bf16_to_device, oracle_operands, compare, assert_within
+from helpers import (bf16_to_device, oracle_operands, compare, assert_within, record, pv_rounding_bound,
+                     assert_within_bound, e4m3_group_max)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +87,72 @@ def test_small_parity_pertensor_descales(pv_mode):
     assert_within(compare(out, lse, ref))
 
 
+def _pertensor_tiles_on_fp8_path(q_codes, lengths, heads, c_of, k_codes=None, lengths_k=None):
+    """The precision guard's decision for every (sequence, head, 128-query tile) in per-tensor mode,
+    recomputed on the host: FP8 scores when c * max|q| * max|k| <= 16, with max|q| the largest code
+    magnitude of the tile's queries and max|k| the largest code of the 16-token groups that hold the
+    sequence's keys (k_codes given: the kernel reads the cast's group maxima), or 448 (c_of(seq,
+    head): the float32 softmax_scale * log2(e) * q_descale * k_descale the kernel forms)."""
+    vals = np.abs(oracle.e4m3_decode(q_codes))
+    gm = None if k_codes is None else oracle.e4m3_decode(e4m3_group_max(k_codes))
+    ok, t0, k0 = [], 0, 0
+    lengths_k = lengths if lengths_k is None else lengths_k
+    for r, L in enumerate(lengths):
+        for hh in range(heads):
+            kb = np.float32(448.0) if gm is None else np.float32(gm[k0 // 16:(k0 + lengths_k[r] - 1) // 16 + 1, hh].max())
+            for q0 in range(0, L, 128):
+                qb = vals[t0 + q0:t0 + min(q0 + 128, L), hh].max()
+                ok.append(np.float32(np.float32(c_of(r, hh)) * np.float32(qb)) * kb <= 16.0)
+        t0 += L
+        k0 += lengths_k[r]
+    return np.array(ok)
+
+
+def _pertensor_run(wl, d, rows=None, k_group_max=False):
+    ops = oracle_operands(wl, "fp8", mode="pertensor", descales=d)
+    dev = torch.device("cuda")
+    mq = lp.VarlenMeta.from_lengths(wl.lengths_q, dev)
+    mk = lp.VarlenMeta.from_lengths(wl.lengths_k, dev)
+    q, k, v = (torch.from_numpy(ops[n]).to(dev) for n in ("pq", "pk", "pv"))
+    t = lambda a: None if a is None else torch.tensor(a, dtype=torch.float32, device=dev)
+    gm = torch.from_numpy(e4m3_group_max(ops["pk"])).to(dev) if k_group_max else None
+    out, lse = lp.lp_attn_varlen_fwd(q, k, v, mq, mk, pv_mode="fp8", q_descale=t(d["q"]), k_descale=t(d["k"]),
+                                     v_descale=t(d["v"]), k_group_max=gm)
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode="fp8",
+                                  q_descale=d["q"], k_descale=d["k"], v_descale=d["v"], rows=rows)
+    return ops, out, lse, ref
+
+
+def _c_of(d, tau=1.0 / math.sqrt(128)):
+    s = np.float32(np.float32(tau) * np.float32(1.0 / math.log(2.0)))
+    g = lambda a, r, hh: np.float32(1.0) if a is None else np.float32(a[r, hh])
+    return lambda r, hh: np.float32(np.float32(s * g(d["q"], r, hh)) * g(d["k"], r, hh))
+
+
+def test_small_parity_pertensor_fp8_scores():
+    """Per-tensor mode with descales that put every query tile on the FP8-score path (k_descale
+    2^-6: K's codes carry the range, so c * max|q| * 448 stays under the guard), element by element
+    against the oracle."""
+    wl = make_custom([260, 70], [190, 300], heads=3, seed=53)
+    rng = np.random.default_rng(54)
+    d = {"q": np.exp2(rng.uniform(-1, 1, (2, 3))), "k": np.full((2, 3), 2.0 ** -6), "v": np.exp2(rng.uniform(-2, 2, (2, 3)))}
+    ops, out, lse, ref = _pertensor_run(wl, d)
+    assert np.all(_pertensor_tiles_on_fp8_path(ops["pq"], wl.lengths_q, 3, _c_of(d)))
+    assert_within(compare(out, lse, ref))
+
+
+def test_pertensor_fp8_scores_full_size(pertensor_wl):
+    """The per-tensor workload (2 x 16384, 24 heads) with k_descale 2^-6: every one of its 6144
+    query tiles takes FP8 scores; sampled rows (every 61st, all heads and keys) against the oracle."""
+    wl = pertensor_wl
+    d = {"q": None, "k": np.full((2, 24), 2.0 ** -6), "v": None}
+    ops, out, lse, ref = _pertensor_run(wl, d, rows=_rows(wl, 61))
+    on_fp8 = _pertensor_tiles_on_fp8_path(ops["pq"], wl.lengths_q, 24, _c_of(d))
+    assert on_fp8.size == 6144 and np.all(on_fp8)
+    assert_within(compare(out, lse, ref))
+
+
 def test_floor_scaled_inputs():
     wl = make_custom([300], [260], heads=2, seed=52)
     out, lse, q, k = _run_mx(wl, "bf16", scaling="floor")
@@ -135,6 +202,27 @@ def test_varlen_sampled(tile_order):
     mask = ~np.isnan(ref.lse[0])
     big_err = np.abs(o[mask] - ref.out[mask]) > 2e-2
     assert np.all(np.abs(ref.out[mask][big_err]) >= 2.0)
+    # and every element within the bound derived from the probabilities' BF16 rounding
+    bound = pv_rounding_bound(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, _rows(wl, 13), "bf16", ref)
+    assert_within_bound(out, ref, bound)
+
+
+def test_varlen_fp8_pv_sampled():
+    """The outlier varlen workload in the fp8 PV mode (E4M3 V, unscaled E4M3 P). As in the mx
+    mode, E4M3 P rounded against the kernel's running maximum and against the oracle's final one
+    differ by more than the plain absolute bound on rows spread over thousands of keys with x20
+    V outliers: every sampled element is held to the bound derived from the oracle's unrounded
+    probabilities (helpers.pv_rounding_bound), LSE to the plain bound."""
+    wl = make_workload("varlen", seed=0)
+    out, lse, _, _ = _run_mx(wl, "fp8")
+    ops = oracle_operands(wl, "fp8")
+    rows = _rows(wl, 13)
+    ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode="fp8", rows=rows)
+    st = compare(out, lse, ref)
+    record(st)
+    assert st["lse_max"] <= 1e-3, st
+    bound = pv_rounding_bound(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, rows, "fp8", ref)
+    assert_within_bound(out, ref, bound)
 
 
 @pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
@@ -168,7 +256,12 @@ def _pertensor_ops(wl, case):
 
 
 @pytest.mark.parametrize("case", ["none", "calibrated", "perhead"])
-def test_pertensor_sampled(pertensor_wl, case):
+@pytest.mark.parametrize("gmax", [False, True])
+def test_pertensor_sampled(pertensor_wl, case, gmax):
+    """The per-tensor workload's descale cases. With K's group maxima (as the cast writes them) the
+    precision guard bounds |k| by the data, and at least 95% of the 6144 query tiles take FP8
+    scores (recomputed on the host); without them it must assume 448 and most tiles take BF16
+    scores. Sampled rows (every 61st, all heads and keys) against the oracle either way."""
     wl = pertensor_wl
     d = wl.descales[case]
     ops = _pertensor_ops(wl, case)
@@ -177,29 +270,38 @@ def test_pertensor_sampled(pertensor_wl, case):
     q = torch.from_numpy(ops["pq"]).to(dev)
     k = torch.from_numpy(ops["pk"]).to(dev)
     v = torch.from_numpy(ops["pv"]).to(dev)
+    gm = torch.from_numpy(e4m3_group_max(ops["pk"])).to(dev) if gmax else None
     t = lambda a: None if a is None else torch.tensor(a, dtype=torch.float32, device=dev)
     out, lse = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=t(d["q"]),
-                                     k_descale=t(d["k"]), v_descale=t(d["v"]))
+                                     k_descale=t(d["k"]), v_descale=t(d["v"]), k_group_max=gm)
     torch.cuda.synchronize()
+    on_fp8 = _pertensor_tiles_on_fp8_path(ops["pq"], wl.lengths_q, 24, _c_of(d), ops["pk"] if gmax else None)
+    record({"case": case, "gmax": gmax, "fp8_tiles": int(on_fp8.sum()), "tiles": int(on_fp8.size)})
+    if gmax:
+        assert on_fp8.mean() >= 0.95, on_fp8.mean()
     ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode="fp8",
-                                  q_descale=d["q"], k_descale=d["k"], v_descale=d["v"], rows=_rows(wl, 509))
+                                  q_descale=d["q"], k_descale=d["k"], v_descale=d["v"], rows=_rows(wl, 61))
     assert_within(compare(out, lse, ref))
 
 
-def test_pertensor_unit_descale_bit_identical(pertensor_wl):
-    """Full size: descale None and a unit descale tensor give the same bits; 2 changes them."""
+@pytest.mark.parametrize("gmax", [False, True])
+def test_pertensor_unit_descale_bit_identical(pertensor_wl, gmax):
+    """Full size: descale None and a unit descale tensor give the same bits; 2 changes them. With
+    K's group maxima the tiles take FP8 scores, without them mostly BF16 scores: both paths."""
     wl = pertensor_wl
     ops = _pertensor_ops(wl, "none")
     dev = torch.device("cuda")
     mq = lp.VarlenMeta.from_lengths(wl.lengths_q, dev)
     q, k, v = (torch.from_numpy(ops[n]).to(dev) for n in ("pq", "pk", "pv"))
-    o0, l0 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8")
+    gm = torch.from_numpy(e4m3_group_max(ops["pk"])).to(dev) if gmax else None
+    o0, l0 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", k_group_max=gm)
     ones = torch.ones((2, 24), dtype=torch.float32, device=dev)
-    o1, l1 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=ones, k_descale=ones, v_descale=ones)
+    o1, l1 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=ones, k_descale=ones, v_descale=ones,
+                                   k_group_max=gm)
     bcast = torch.ones((1, 1), dtype=torch.float32, device=dev)
     o2, l2 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=bcast, k_descale=bcast,
-                                   v_descale=bcast)
-    o3, l3 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=2.0)
+                                   v_descale=bcast, k_group_max=gm)
+    o3, l3 = lp.lp_attn_varlen_fwd(q, k, v, mq, mq, pv_mode="fp8", q_descale=2.0, k_group_max=gm)
     torch.cuda.synchronize()
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
     assert torch.equal(o0.view(torch.int16), o2.view(torch.int16)) and torch.equal(l0, l2)
@@ -411,3 +513,26 @@ def test_k_group_max_same_results(pv_mode, which):
     with pytest.raises(ValueError):
         bad = lp.Mxfp8Tensor(k.payload, k.scales, mk, k.group_max[:1])
         lp.lp_attn_varlen_fwd(q, bad, v, mq, mk, pv_mode=pv_mode)
+
+
+@pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
+def test_fp8_score_guard_threshold_selects_the_path(pv_mode):
+    """fp8_score_guard picks the score path: a negative threshold forces BF16 scores, a huge one
+    FP8 scores, on the same dense inputs (where the default takes FP8). Both match the oracle;
+    the default equals the forced-FP8 run bit for bit and differs from the forced-BF16 one (the
+    FP8 instruction truncates inside its groups of 8 products)."""
+    wl = make_workload("dense", seed=0)
+    outs = {}
+    for name, g in (("default", None), ("never", -1.0), ("always", 1e30)):
+        o, l, _, _ = _run_mx(wl, pv_mode, fp8_score_guard=g)
+        outs[name] = (o.clone(), l.clone())
+    ops = oracle_operands(wl, pv_mode)
+    ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode=pv_mode,
+                                  rows=_rows(wl, 31))
+    for name in outs:
+        assert_within(compare(*outs[name], ref))
+    assert torch.equal(outs["default"][0].view(torch.int16), outs["always"][0].view(torch.int16))
+    assert not torch.equal(outs["default"][1], outs["never"][1])
+    with pytest.raises(ValueError):
+        _run_mx(wl, pv_mode, fp8_score_guard=0.0)
+

@@ -219,3 +219,26 @@ def test_group_max_optional():
     torch.cuda.synchronize()
     assert b.group_max is None
     assert torch.equal(a.payload, b.payload) and torch.equal(a.scales, b.scales)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cast_group_max(dtype):
+    """The cast's optional group maxima: per 16 tokens and head, the largest code magnitude, equal to
+    the NumPy maximum over the oracle's codes (a ragged last group included); the codes are the
+    plain cast's, bit for bit."""
+    from helpers import e4m3_group_max
+    rng = np.random.default_rng(1400)
+    t, h = 1000 + 13, 3
+    x = rng.standard_normal((t, h, 128)).astype(np.float32) * np.exp2(rng.integers(-12, 9, size=(t, h, 1))).astype(np.float32)
+    x[rng.random(x.shape) < 1e-4] = 500.0                                 # saturating values
+    xt = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+        x = xt.float().cpu().numpy()
+    gm = torch.empty(lp.e4m3_group_max_shape(t, h), dtype=torch.uint8, device="cuda")
+    codes = lp.cast_e4m3(xt, group_max_out=gm)
+    plain = lp.cast_e4m3(xt)
+    torch.cuda.synchronize()
+    ref_codes = oracle.e4m3_cast(x.astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), ref_codes) and torch.equal(codes, plain)
+    assert np.array_equal(gm.cpu().numpy(), e4m3_group_max(ref_codes))
