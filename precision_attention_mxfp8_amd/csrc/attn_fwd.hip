@@ -65,8 +65,9 @@
 // here. Typical N(0,1) data stays on the FP8 path; tiles whose rows meet outliers take the BF16
 // path.
 //
-// Workgroup ids are remapped so that consecutive tiles of one (sequence, head) land on the same
-// XCD (ids are dealt round-robin over the 8 XCDs), sharing K/V in that XCD's L2.
+// Workgroup ids are remapped so that all tiles of one (sequence, head) land on the same XCD (ids
+// are dealt round-robin over the 8 XCDs), sharing K/V in that XCD's L2; with a head count that is
+// a multiple of 8, head h goes to XCD h % 8, where the preparation kernels wrote its codes.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <stdint.h>
@@ -206,12 +207,16 @@ template <>
 struct PFrag<false> { uint32_t w[4][2][4]; };
 
 // MX: Q and K carry E8M0 block scales. FP8V: V is E4M3 (two wave groups). VMX: that E4M3 V
-// carries E8M0 scales per 32 tokens (the P V instruction's A-operand scales). QB: Q and K are
+// carries E8M0 scales per 32 tokens (the P V instruction's A-operand scales). DQ: the guarded
+// path of the BF16-V kernel: MX Q and K dequantized exactly to BF16 (Q once per tile into
+// registers, K once per block into BF16 LDS tiles), then the BF16 pipeline below. QB: Q and K are
 // BF16 (the BF16 FlashAttention forward: BF16 scores and BF16 P V, one wave group).
-template <bool MX, bool FP8V, bool VMX, bool QB = false>
+template <bool MX, bool FP8V, bool VMX, bool QB = false, bool DQ = false>
 struct Attn {
   static_assert(!QB || (!MX && !FP8V && !VMX), "BF16 Q/K come with BF16 V only");
-  using L = Lay<FP8V, QB>;
+  static_assert(!DQ || (MX && !FP8V && !VMX && !QB), "the dequantized path is the BF16-V kernel's");
+  static constexpr bool KB16 = QB || DQ;  // K in LDS and Q in registers are BF16
+  using L = Lay<FP8V, KB16>;
   using PF = PFrag<FP8V>;
   static constexpr int G = Groups<FP8V>::G;
 
@@ -237,7 +242,9 @@ struct Attn {
 
   // ---- per-wave state ----
   int qsc[2];
-  v8bf qb16[2][4];           // QB: Q fragments, query tile nt, head_dim slice 32u .. 32u + 31
+  v8bf qb16[2][4];           // QB, DQ: Q fragments, query tile nt, head_dim slice 32u .. 32u + 31
+  uint4 kpre[4];             // DQ: this lane's staged K chunks of the next block (FP8), and
+  uint32_t kpre_sc[4];       // their rows' scale words
   float qbound;              // max |q| bound of the wave's queries
   uint32_t ksw[8];           // first batch of the guard's K scale words, loaded before Q
   const uint8_t* qrow[2];    // this lane's query rows (nullptr past the end)
@@ -385,6 +392,39 @@ struct Attn {
       for (int i = 0; i < N; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(dst + i * 1024), 16,
                                                  off0 + (uint32_t)(ROWS * i) * (uint32_t)v_st_b, 0, 0, 0);
+    }
+  }
+
+  // ---------------------------------------------------------------- DQ: K dequantized into BF16 LDS
+  // Block b of K (FP8 payload and scale words) into registers: lane L of wave w stages 16-byte
+  // chunk L % 8 of key rows 32w + 8i + L / 8 (i = 0..3) and those rows' scale words. Buffer loads
+  // whose range ends at the tensor's last byte: rows past the end read zeros (and are masked).
+  __device__ __forceinline__ void dq_load_k(int b) {
+    const auto r = rsrc(kbase + (int64_t)(b * BN + 32 * wave) * k_st_b, p.k_end);
+    const int r8 = lane >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + r8;
+      kpre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              r, (int)((uint32_t)(row * (int)k_st_b) + 16u * (lane & 7)), 0, 0));
+      // the scale storage is padded to whole 128-row blocks per sequence: every row exists
+      kpre_sc[i] = *reinterpret_cast<const uint32_t*>(ksc_base + (int64_t)(b * BN + 32 * wave + row) * H * 4);
+    }
+  }
+
+  // The staged chunks, dequantized exactly (E4M3 times the block's power of two) to BF16, into K
+  // buffer buf in the BF16 layout that the scores read: row r holds 16 chunks of 8 elements, chunk c
+  // at position c ^ (r % 16). A staged 16-byte FP8 chunk c8 becomes BF16 chunks 2 c8 and 2 c8 + 1.
+  __device__ __forceinline__ void dq_store_k(int buf) {
+    const int r8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * wave + 8 * i + r8;
+      const float sc = e8m0_to_float((kpre_sc[i] >> (8 * (c8 >> 1))) & 0xFFu);   // block c8 / 2 of the row
+      const v8bf lo = fp8x8_to_bf16(kpre[i].x, kpre[i].y, sc), hi = fp8x8_to_bf16(kpre[i].z, kpre[i].w, sc);
+      const uint32_t base = L::OFF_K + buf * L::K_BYTES + row * 256;
+      *reinterpret_cast<LDS v8bf*>(dyn() + opaque(base + 16 * ((2 * c8) ^ (row & 15)))) = lo;
+      *reinterpret_cast<LDS v8bf*>(dyn() + opaque(base + 16 * ((2 * c8 + 1) ^ (row & 15)))) = hi;
     }
   }
 
@@ -835,12 +875,12 @@ struct Attn {
     LDS uint8_t* v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     v8i qf[2];
-    if (DO_QK && !QB) {
+    if (DO_QK && !KB16) {
       qf[0] = q_frag(0);
       qf[1] = q_frag(1);
     }
-    LDS const v8bf* kq[4];  // QB: this lane's slice-u chunk of key row n16 (row 16t + n16: + t * 4096 bytes)
-    if constexpr (QB) {
+    LDS const v8bf* kq[4];  // QB, DQ: this lane's slice-u chunk of key row n16 (row 16t + n16: + t * 4096 bytes)
+    if constexpr (KB16) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         kq[u] = reinterpret_cast<LDS const v8bf*>(dyn() + opaque(L::OFF_K + kb1 * L::K_BYTES + n16 * 256 +
@@ -870,7 +910,7 @@ struct Attn {
           pf_cur.w[k >> 1][nt][2 * (k & 1) + 1] = cvt_pk_bf16(s[k][nt][2], s[k][nt][3]);
         }
       }
-      if (DO_QK && QB) {  // BF16 scores of block j+1, key tile k
+      if (DO_QK && KB16) {  // BF16 scores of block j+1, key tile k
         v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -908,10 +948,17 @@ struct Attn {
   // PAR = j % 2 (a constant: the V buffers are chosen at compile time).
   template <bool FAST, bool FIRST, bool LAST, int PAR>
   __device__ __forceinline__ void iteration1(int j, v4f s[8][2], const PF& pf_prev, PF& pf_cur) {
-    if (j + 2 < ng) dma_k(0, blk(j + 2), j & 1);
+    if constexpr (DQ) {
+      if (j + 2 < ng) dq_load_k(blk(j + 2));
+    } else {
+      if (j + 2 < ng) dma_k(0, blk(j + 2), j & 1);
+    }
     dma_v(PAR, blk(j), 0);
     step<FAST && !LAST, !FIRST, LAST, PAR>(j, s, pf_prev, pf_cur);
     if (!FAST && !LAST) scores_bf16((j + 1) & 1, s);
+    if constexpr (DQ) {  // block j+2's K, staged in registers during the step, into K buffer j % 2
+      if (j + 2 < ng) dq_store_k(j & 1);
+    }
     wait_vm_all();
     __syncthreads();
   }
@@ -959,7 +1006,7 @@ struct Attn {
     int j = 0;
     if constexpr (G == 1) {
       if (ng > 0) {
-        if constexpr (QB)
+        if constexpr (KB16)
           scores_qb(0, s);
         else if (FAST)
           scores_fp8(0, s);
@@ -1096,10 +1143,11 @@ struct Attn {
   // One query tile. The precision guard decides before the key loop between FP8 and BF16
   // scores. MODE 2: both loops in this function. MODE 0: FP8 scores only; when the guard fails,
   // every wave returns false with no load in flight and nothing written, and the caller runs the
-  // tile again with MODE 1 (BF16 scores, no guard), which always completes and returns true.
+  // tile again with MODE 1 (BF16 scores, no guard: the two-group kernel's BF16 score loop, or
+  // the DQ pipeline for the BF16-V kernel), which always completes and returns true.
   template <int MODE>
   __device__ __forceinline__ bool run(int qtile) {
-    constexpr bool GUARD = MODE != 1 && !QB;  // this call evaluates the guard (BF16 Q/K need none)
+    constexpr bool GUARD = MODE != 1 && !KB16;  // this call evaluates the guard (BF16 scores need none)
     constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
     H = p.num_heads;
     qtile0 = qtile;
@@ -1137,7 +1185,9 @@ struct Attn {
     if (GUARD && (MX || kgm_base != nullptr)) guard_prefetch();
 
     // start the first loads before touching Q
-    if (ng > 0) {
+    if constexpr (DQ) {
+      if (ng > 0) dq_load_k(blk(0));  // stored as BF16 once Q's loads have gone out
+    } else if (ng > 0) {
       if (grp == 0) {
         dma_k(0, blk(0), 0);
         if (ng > 1) dma_k(0, blk(1), 1);
@@ -1147,8 +1197,31 @@ struct Attn {
       }
     }
 
-    // ---- Q fragments: BF16 in registers (QB), or FP8 (score B operand) through LDS; the
-    // guarded path reloads FP8 Q as BF16 ----
+    // ---- Q fragments: BF16 in registers (QB; DQ: dequantized exactly), or FP8 (score B operand)
+    // through LDS; the guarded path of the two-group kernel reloads FP8 Q as BF16 ----
+    if constexpr (DQ) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int qi = q0 + wave * 32 + nt * 16 + n16;
+        const bool in = qi < Lq;
+        const int qc = in ? qi : Lq - 1;
+        const uint8_t* qp = p.q + (int64_t)(q_start + qc) * p.q_st + (int64_t)head * p.q_sh;
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)scq + qc) * H + head) * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint2 w = ldg8(qp + 32 * u + 8 * g);  // head_dim 32u + 8g .. 32u + 8g + 7: scale block u
+          if (!in) w = make_uint2(0, 0);
+          qb16[nt][u] = fp8x8_to_bf16(w.x, w.y, e8m0_to_float((sw >> (8 * u)) & 0xFFu));
+        }
+      }
+      if (ng > 0) {
+        dq_store_k(0);
+        if (ng > 1) {
+          dq_load_k(blk(1));
+          dq_store_k(1);
+        }
+      }
+    }
     if constexpr (QB) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -1169,7 +1242,7 @@ struct Attn {
     uint32_t qmax_code = 0, qmax_scale = 0;
     v8i qf[2];
 #pragma unroll
-    for (int nt = 0; nt < 2 && !QB; ++nt) {
+    for (int nt = 0; nt < 2 && !KB16; ++nt) {
       const int qi = q0 + wave * 32 + nt * 16 + n16;
       const bool in = qi < Lq;
       const int qc = in ? qi : Lq - 1;
@@ -1195,7 +1268,7 @@ struct Attn {
       }
       qmax_scale = max(qmax_scale, in ? (uint32_t)qsc[nt] : 0u);
     }
-    if (grp == 0 && !QB) {  // both groups hold the same queries: group 0 stores the fragments
+    if (grp == 0 && !KB16) {  // both groups hold the same queries: group 0 stores the fragments
       LDS v4u_t* qa = lds_at<v4u_t>(lds_base + L::OFF_Q + wave * 2 * 2048 + lane * 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -1225,14 +1298,15 @@ struct Attn {
       if (GUARD) guard_publish(red);
       wait_vm_all();
       __syncthreads();
-      if constexpr (QB) {
+      if constexpr (KB16) {
         main_loop<true>(niter);
-      } else if (MODE == 1) {
+      } else if constexpr (MODE == 1) {
         main_loop<false>(niter);
+      } else if constexpr (MODE == 0) {
+        if (!fp8_scores_ok_tile(red)) return false;  // uniform: every wave reads the same slots
+        main_loop<true>(niter);
       } else {
-        const bool fast = fp8_scores_ok_tile(red);  // uniform: every wave reads the same slots
-        if (MODE == 0 && !fast) return false;
-        if (fast) main_loop<true>(niter); else main_loop<false>(niter);
+        if (fp8_scores_ok_tile(red)) main_loop<true>(niter); else main_loop<false>(niter);
       }
     }
 
@@ -1298,6 +1372,17 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
     seq = p.tile_order[3 * blockIdx.x];
     head = p.tile_order[3 * blockIdx.x + 1];
     qtile = p.tile_order[3 * blockIdx.x + 2];
+  } else if ((p.num_heads & 7) == 0) {
+    // head h on XCD h % 8 (workgroup ids are dealt round-robin over the 8 XCDs): the XCD whose
+    // workgroups quantized that head's Q and K and cast its V (their groups enumerate heads
+    // fastest), so the codes they just wrote are in that XCD's L2; the XCD's tiles in (sequence,
+    // head, tile) order. The grid is exactly num_seqs * num_heads * q_tiles.
+    const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+    qtile = k % p.q_tiles;
+    const int rest = k / p.q_tiles, hx = p.num_heads >> 3;
+    head = x + 8 * (rest % hx);
+    seq = rest / hx;
+    if (seq >= p.num_seqs) return;
   } else {
     const int per_xcd = (int)(gridDim.x >> 3);  // grid is a multiple of 8
     const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
@@ -1315,9 +1400,20 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
   a.head = head;
   a.load_meta();
   if (qtile * BM >= a.Lq) return;
-  if constexpr (Groups<FP8V>::G == 1) {
+  if constexpr (Groups<FP8V>::G == 1 && !(MX && !QB)) {
     a.template run<2>(qtile);  // 512 registers per wave: both score loops fit in one allocation
+  } else if constexpr (Groups<FP8V>::G == 1) {
+    // BF16 V with MX Q/K: a tile that fails the guard runs the DQ pipeline (K dequantized once per
+    // block into BF16 LDS tiles, Q into BF16 registers), inline: 512 registers hold both paths
+    if (!a.template run<0>(qtile)) {
+      Attn<MX, false, false, false, true> d(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
+      d.seq = seq;
+      d.head = head;
+      d.load_meta();
+      d.template run<1>(qtile);
+    }
   } else if (!a.template run<0>(qtile)) {
+    // guard failed: the two-group kernel's BF16 score loop, in a function of its own
     // The parameters are the kernel's only argument: the callee reads them in place in the
     // kernel-argument segment (taking the address of p instead makes the kernel itself read its
     // fields differently, to the FP8 loop's cost). The host compilation pass has no such segment.
@@ -1334,7 +1430,9 @@ template <bool MX, bool FP8V, bool VMX, bool QB = false>
 hipError_t launch_variant(const AttnParams& p, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // Raising the dynamic LDS limit is a per-kernel, per-device attribute: done once per device.
   static std::atomic<uint64_t> configured{0};
-  const int bytes = Lay<FP8V, QB>::TOTAL;
+  // the BF16-V kernel with MX Q/K also runs guard-failing tiles on BF16 K tiles (DQ): room for both
+  constexpr int b0 = Lay<FP8V, QB>::TOTAL, b1 = Lay<FP8V, true>::TOTAL;
+  const int bytes = (MX && !FP8V && !QB && b1 > b0) ? b1 : b0;
   const dim3 block(256 * Groups<FP8V>::G);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

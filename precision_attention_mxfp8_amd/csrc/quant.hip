@@ -221,11 +221,12 @@ __device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
 }
 
-// The cast with group maxima (per-tensor K for the attention's precision guard): a workgroup
-// owns 16 consecutive tokens of one head (bid enumerates (16-token group, head), heads fastest),
-// 16 lanes per token as in cast_block, and writes the largest code magnitude of its 2048 codes
-// (codes order like magnitudes, and the RNE conversion is monotonic, so that is the code of
-// the largest clamped magnitude). Tokens past the end are not read and count as zero.
+// The cast by (16-token group, head): a workgroup owns 16 consecutive tokens of one head (bid
+// enumerates (16-token group, head), heads fastest, as the quantizer's groups do), 16 lanes per
+// token as in cast_block. With group maxima (per-tensor K for the attention's precision guard) it
+// also writes the largest code magnitude of its 2048 codes (codes order like magnitudes, and the
+// RNE conversion is monotonic, so that is the code of the largest clamped magnitude). Tokens
+// past the end are not read and count as zero.
 template <typename T>
 __device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid, float* red) {
   const int h = (int)(bid % (unsigned)p.num_heads);
@@ -243,6 +244,7 @@ __device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid, fl
     const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
     *reinterpret_cast<uint2*>(p.y + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
   }
+  if (p.group_max == nullptr) return;  // uniform over the workgroup
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -268,14 +270,18 @@ __global__ __launch_bounds__(256) void e4m3_cast_gmax_kernel(CastParams p) {
 // V's unscaled E4M3 cast. Each of these passes moves ~12 MB at the dense shape, too little for
 // one launch to get past its ramp-up and tail; one grid over all three amortizes them. Workgroup
 // ranges: [0, nq) Q, [nq, nq + nk) K, then V; each workgroup runs one pass's body unchanged.
+// V takes the (16-token group, head) mapping of the quantizer's groups, so with a head count that
+// is a multiple of 8 every head's Q, K and V codes are written by workgroups of one XCD (ids are
+// dealt round-robin over the 8 XCDs), the XCD whose L2 the attention kernel reads that head from.
 template <typename T>
 __global__ __launch_bounds__(256) void prepare_qkv_kernel(QuantParams pq, QuantParams pk, CastParams pv, unsigned nq,
                                                           unsigned nk) {
   __shared__ uint32_t red[4];
+  __shared__ float fred[4];
   const unsigned b = blockIdx.x;
   if (b < nq) quantize_group<T>(pq, b, red);
   else if (b < nq + nk) quantize_group<T>(pk, b - nq, red);
-  else cast_block<T>(pv, b - nq - nk);
+  else cast_group<T>(pv, b - nq - nk, fred);
 }
 
 // ---- per-tensor current scaling (TensorRT-LLM TE-backend PR: Q/K/V and O scales written from
@@ -421,7 +427,7 @@ hipError_t launch_quantize_tokens(const QuantParams& p, hipStream_t s) {
 
 hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, const CastParams& pv, hipStream_t s) {
   const int64_t nq = pq.total_scale_rows / 16 * pq.num_heads, nk = pk.total_scale_rows / 16 * pk.num_heads;
-  const int64_t nv = (pv.total_tokens * pv.num_heads * 16 + 255) / 256;
+  const int64_t nv = (pv.total_tokens + 15) / 16 * pv.num_heads;  // (16-token group, head) workgroups
   if (nq + nk + nv == 0) return hipSuccess;
   const dim3 grid((unsigned)(nq + nk + nv));
   if (pq.x_dtype == LPFA_DTYPE_BF16)

@@ -51,12 +51,15 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("scores", ["guarded", "bf16"])
 @pytest.mark.parametrize("pv_mode", ["bf16", "fp8"])
 @pytest.mark.parametrize("case", range(len(SMALL)))
-def test_small_parity_mx(pv_mode, case):
+def test_small_parity_mx(pv_mode, case, scores):
+    """Every element against the oracle. scores="bf16" forces the BF16 score path (fp8_score_guard
+    < 0): the dequantized-K pipeline with BF16 V, the two-group kernel's BF16 score loop with E4M3 V."""
     lq, lk, h = SMALL[case]
     wl = make_custom(lq, lk, heads=h, seed=40 + case)
-    out, lse, q, k = _run_mx(wl, pv_mode)
+    out, lse, q, k = _run_mx(wl, pv_mode, fp8_score_guard=None if scores == "guarded" else -1.0)
     ops = oracle_operands(wl, pv_mode)
     assert np.array_equal(q.payload.cpu().numpy(), ops["pq"]) and np.array_equal(q.scales.cpu().numpy(), ops["sq"])
     ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode=pv_mode)
