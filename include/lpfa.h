@@ -39,6 +39,9 @@
  *     caller's next synchronisation, as for any asynchronous launch.
  *   - Entry points are thread-safe; concurrent calls on different streams do not
  *     share state.
+ *   - With LPFA_LOG=1 in the environment, the first lp_attn_varlen_fwd call of each variant
+ *     in the process prints one line to stderr naming the Q/K and V types fed to the kernel
+ *     (FastVideo fp8-PV PR: a once-per-process log of the V dtype the attention received).
  */
 #ifndef LPFA_H
 #define LPFA_H

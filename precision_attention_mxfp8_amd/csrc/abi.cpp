@@ -1,7 +1,10 @@
 // C ABI entry points (include/lpfa.h): host checks, then one launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "kernels.h"
@@ -14,6 +17,27 @@ int launch_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return LPFA_OK;
   lpfa::set_error(std::string(what) + " launch failed: " + hipGetErrorString(e));
   return LPFA_EIO;
+}
+
+// With LPFA_LOG=1 in the environment, the first launch of each forward variant in the process
+// prints one line to stderr naming the operand types actually fed to the kernel (FastVideo fp8-PV
+// PR: a once-per-process log of the V dtype that reached the attention kernel).
+void log_variant_once(const lpfa_attn_args* a) {
+  static const bool on = [] {
+    const char* e = std::getenv("LPFA_LOG");
+    return e != nullptr && e[0] == '1';
+  }();
+  if (!on) return;
+  const int qk = a->qk_bf16 ? 2 : (a->q_scale != nullptr ? 0 : 1);
+  const int key = qk * 3 + a->pv_mode;  // pv_mode in 0..2 after validation
+  static std::atomic<uint32_t> seen{0};
+  if (seen.fetch_or(1u << key) & (1u << key)) return;
+  static const char* const qk_name[] = {"MXFP8 (E4M3, E8M0 per 32 along head_dim)", "E4M3 per-tensor", "BF16"};
+  static const char* const v_name[] = {"BF16 (P rounded to BF16)", "E4M3 unscaled, dequant scale 1.0 (P unscaled E4M3)",
+                                       "MXFP8 along tokens (P unscaled E4M3)"};
+  std::fprintf(stderr, "lpfa: lp_attn_varlen_fwd: Q/K %s, V %s, descales q/k/v %s/%s/%s\n", qk_name[qk],
+               v_name[a->pv_mode], a->q_descale ? "yes" : "none", a->k_descale ? "yes" : "none",
+               a->v_descale ? "yes" : "none");
 }
 
 }  // namespace
@@ -202,6 +226,7 @@ int lp_fp8_cast_current_noalloc(const void* x, int x_dtype, int64_t stride_tok, 
 
 int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
   if (int rc = lpfa::check_attn(a)) return rc;
+  log_variant_once(a);
   lpfa::AttnParams p{};
   p.q = a->q;
   p.k = a->k;
