@@ -37,11 +37,12 @@ __device__ __forceinline__ uint32_t cvt4_e4m3_over(uint32_t old, float a, float 
 
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
-// Two floats -> two BF16 (round to nearest even) packed in one word, first in the low half.
+// Two floats -> two BF16 (round to nearest even) packed in one word, first in the low half: one
+// v_cvt_pk_bf16_f32 (element-wise casts would convert each value alone and then shift and merge).
+typedef float cvt_f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 cvt_bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  uint16_t ua = __builtin_bit_cast(uint16_t, ha), ub = __builtin_bit_cast(uint16_t, hb);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(cvt_f32x2_t{a, b}, cvt_bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
