@@ -14,11 +14,11 @@
 //  * bwd_dequant_kernel: Qd, Qt, Kd, Vd and Kt dequantized once into BF16 copies in the caller's
 //    workspace (the main kernels re-read every tile once per 64-row block of the other side).
 //    The same launch computes D for every (head, query) into the workspace (16 lanes per row).
-//  * bwd_dkdv_kernel: one workgroup = (64 keys of one sequence, head), 4 waves x 16 keys. The
+//  * bwd_dkdv_kernel: one workgroup = (128 keys of one sequence, head), 4 waves x 32 keys. The
 //    keys' K and V fragments and the dK, dV accumulators stay in registers while the workgroup
 //    walks the sequence's queries 64 at a time. The epilogue writes BF16, or quantizes each
 //    32-element block to MXFP8 with the quantizer's exponent rule (and writes pad scale rows).
-//  * bwd_dq_kernel: one workgroup = (64 queries, head), 4 waves x 16 queries, walking the keys.
+//  * bwd_dq_kernel: one workgroup = (128 queries, head), 4 waves x 32 queries, walking the keys.
 //    dQ has its own pass instead of atomics from the dK/dV pass, so every result is independent
 //    of scheduling; the price is recomputing S and dP.
 //
@@ -37,11 +37,14 @@
 // LDS tiles are 64 rows x 128 BF16 (256-byte rows) with 16-byte chunk c of row r stored at
 // chunk c ^ (r & 15): a row read (one chunk of 16 rows) and a transposing read (two chunks of 16
 // rows) both spread over the banks. Tiles arrive by 16-byte direct-to-LDS loads from the BF16
-// copies (single-buffered; two workgroups per CU overlap one's loads with the other's work), and
-// fragment reads are issued in groups ahead of the matrix instructions that use them.
+// copies (double-buffered: the next step's tiles load while the current step computes), and
+// fragment reads are issued in groups ahead of the matrix instructions that use them. Each wave
+// owns two 16-row tiles of its own side, so every fragment it reads from LDS feeds two matrix
+// instructions (LDS bandwidth, not the matrix core, bounds a one-tile-per-wave loop).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -57,12 +60,15 @@ typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));  // LDS accesses use ext vectors: HIP's
                                                              // uint4 does not bind to LDS references
 
-constexpr int BR = 64;                     // rows (keys or queries) per workgroup and per step
-constexpr int TILE = BR * 256;             // one BF16 tile
-constexpr int OFF_VEC = 3 * TILE;          // dK/dV pass: LSE (log2 units) and D of the step's queries
-constexpr int LDS_BYTES = 3 * TILE + 2 * BR * 4;
+constexpr int BR = 64;                     // rows of the other side per step (staged tiles)
+constexpr int WR = 32;                     // rows of the workgroup's own side per wave: two 16-row tiles
+constexpr int BO = 4 * WR;                 // own-side rows per workgroup
+constexpr int TILE = BR * 256;             // one staged BF16 tile
+constexpr int STAGE = 3 * TILE;            // the three tiles of one step (double-buffered)
+constexpr int OFF_VEC = 2 * STAGE;         // dK/dV pass: LSE (log2 units) and D of a step's queries, per buffer
+constexpr int LDS_BYTES = 2 * STAGE + 2 * 2 * BR * 4;
 constexpr float LOG2E = 1.4426950408889634f;
-static_assert(BR * 128 * 4 <= 3 * TILE, "the FP32 epilogue tile fits in the staging area");
+static_assert(BO * 128 * 4 <= 2 * STAGE, "the FP32 epilogue tile fits in the staging area");
 
 // E8M0 byte -> 2^(b - 127) as a float (b = 0 gives the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_f(uint32_t b) {
@@ -159,6 +165,21 @@ __device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
 // Ends a scheduling group: the fragment reads written before it are issued together, and the
 // matrix instructions that use them follow (one wait for the group instead of one per read).
 __device__ __forceinline__ void group_end() { __builtin_amdgcn_sched_barrier(0); }
+
+// (row block, head) of this workgroup in a one-dimensional grid of nblk * H workgroups. Workgroup
+// ids are dealt round-robin over the 8 XCDs; with H a multiple of 8, head h runs on XCD h % 8, so
+// the other side's tiles of a head, which every row block of that head reads, stay in one L2.
+__device__ __forceinline__ void block_head(int nblk, int H, int& blk, int& head) {
+  const int L = (int)blockIdx.x;
+  if ((H & 7) == 0) {
+    const int k = L >> 3;
+    head = (L & 7) + 8 * (k / nblk);
+    blk = k % nblk;
+  } else {
+    head = L / nblk;
+    blk = L % nblk;
+  }
+}
 
 // ---- D = rowsum(dO * O)
 
@@ -266,47 +287,53 @@ __device__ __forceinline__ void emit_rows(LDS float* ep, uint8_t* dst, uint8_t* 
   dst_scale[((srow0 + r) * H + head) * 4 + c4] = sbyte;
 }
 
-// accumulators (result layout: lane (g, c) holds rows 4g+i of wave w's 16, column 16dt + c)
-// -> FP32 tile in LDS, times `mul`
-__device__ __forceinline__ void acc_to_lds(LDS float* ep, const v4f acc[8], float mul, int wave, int g, int n16) {
+// accumulators of the wave's two 16-row tiles (result layout: lane (g, c) holds rows 16t + 4g + i
+// of wave w's 32, column 16dt + c) -> FP32 tile of BO rows in LDS, times `mul`
+__device__ __forceinline__ void acc_to_lds(LDS float* ep, const v4f acc[2][8], float mul, int wave, int g, int n16) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ep[(16 * wave + 4 * g + i) * 128 + 16 * dt + n16] = acc[dt][i] * mul;
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ep[(WR * wave + 16 * t + 4 * g + i) * 128 + 16 * dt + n16] = acc[t][dt][i] * mul;
 }
 
 // ---- dK, dV
+// One workgroup = BO keys of one (sequence, head); wave w owns keys 32w + 16t + n (t = 0, 1): their
+// K and V fragments and dK, dV accumulators stay in registers while the workgroup walks the
+// sequence's queries 64 at a time. Every fragment read from LDS feeds both key tiles. The next
+// step's Q, dO and Qt tiles load (into the other buffer) while the current step computes.
 
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
-  LDS uint8_t* lds = (LDS uint8_t*)smem;
-  LDS uint8_t* tq = lds;             // Q (head_dim orientation), BF16
-  LDS uint8_t* tdo = lds + TILE;     // dO
-  LDS uint8_t* tqt = lds + 2 * TILE; // Q (token orientation), BF16
-  LDS float* vec = reinterpret_cast<LDS float*>(lds + OFF_VEC);  // [0, 64): LSE * log2 e; [64, 128): D
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_dyn[];
+  LDS uint8_t* lds = (LDS uint8_t*)smem_dyn;
 
-  const int H = p.num_heads, head = blockIdx.y;
-  const int row0 = blockIdx.x * BR;  // row of K's padded scale storage
+  const int H = p.num_heads;
+  int blk, head;
+  block_head((int)(p.rows_k / BO), H, blk, head);
+  const int row0 = blk * BO;  // row of K's padded scale storage (sequences are padded to 128)
   const int seq = find_seq(p.cu_scale_k, p.num_seqs, row0);
   const int srow_k = p.cu_scale_k[seq];
   const int k_loc = row0 - srow_k;
   const int kbase = p.cu_k[seq], Lk = p.cu_k[seq + 1] - kbase;
   const int qbase = p.cu_q[seq], Lq = p.cu_q[seq + 1] - qbase;
-  const int srow_q = p.cu_scale_q[seq];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  v4f dv[8], dk[8];
+  v4f dv[2][8], dk[2][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) dv[dt] = dk[dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) dv[t][dt] = dk[t][dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (k_loc < Lk && Lq > 0) {
-    // this lane's key (B operand column n16 of the wave's 16): K and V fragments, k = d
-    const int kr = min(k_loc + 16 * wave + n16, Lk - 1);
-    const int64_t tk = kbase + kr;
-    v8bf kf[4], vf[4];
-    {
+    // this lane's keys (B operand column n16 of tile t): K and V fragments, k = d
+    v8bf kf[2][4], vf[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = min(k_loc + WR * wave + 16 * t + n16, Lk - 1);
+      const int64_t tk = kbase + kr;
       const uint8_t* kp = p.k + (tk * H + head) * 128 + 8 * g;
       const uint8_t* vp = p.v + (tk * H + head) * 128 + 8 * g;
       const uint8_t* ks = p.k_scale + ((int64_t)(srow_k + kr) * H + head) * 4;
@@ -315,203 +342,298 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       for (int u = 0; u < 4; ++u) {
         const uint2 wk = *reinterpret_cast<const uint2*>(kp + 32 * u);
         const uint2 wv = *reinterpret_cast<const uint2*>(vp + 32 * u);
-        kf[u] = __builtin_bit_cast(v8bf, fp8x8_bf16(wk.x, wk.y, e8m0_f(ks[u])));
-        vf[u] = __builtin_bit_cast(v8bf, fp8x8_bf16(wv.x, wv.y, e8m0_f(vs[u])));
+        kf[t][u] = __builtin_bit_cast(v8bf, fp8x8_bf16(wk.x, wk.y, e8m0_f(ks[u])));
+        vf[t][u] = __builtin_bit_cast(v8bf, fp8x8_bf16(wv.x, wv.y, e8m0_f(vs[u])));
       }
     }
     const float c = p.softmax_scale * LOG2E;
     const int nqb = (Lq + BR - 1) / BR;
-
     const int64_t qelems = p.total_q * H * 128;
-    for (int j = 0; j < nqb; ++j) {
+    LDS float* vec0 = reinterpret_cast<LDS float*>(lds + OFF_VEC);  // per buffer: [0, 64) LSE, [64, 128) D
+    const float* lse_h = p.lse + (int64_t)head * p.total_q + qbase;
+    const float* del_h = p.delta + (int64_t)head * p.total_q + qbase;
+
+    // step j's Q, dO and Qt tiles, and its queries' LSE (wave 0) and D (wave 1), into buffer buf
+    // (query rows past the sequence read its last row; their P is masked to 0 where it is used)
+    auto stage = [&](int j, int buf) {
       const int64_t t0 = qbase + (int64_t)j * BR;
       const int nr = Lq - j * BR;
-      stage_tile(tq, p.qd16, p.qd16 + qelems, t0, nr, H, head, wave, lane);
-      stage_tile(tdo, p.dout, p.dout + qelems, t0, nr, H, head, wave, lane);
-      stage_tile(tqt, p.qt16, p.qt16 + qelems, t0, nr, H, head, wave, lane);
-      if (tid < BR) {
-        const int qv = j * BR + tid;
-        const int64_t t2 = qbase + min(qv, Lq - 1);
-        vec[tid] = qv < Lq ? p.lse[(int64_t)head * p.total_q + t2] * LOG2E : __builtin_inff();
-        vec[BR + tid] = qv < Lq ? p.delta[(int64_t)head * p.total_q + t2] : 0.0f;
+      LDS uint8_t* b = lds + buf * STAGE;
+      stage_tile(b, p.qd16, p.qd16 + qelems, t0, nr, H, head, wave, lane);
+      stage_tile(b + TILE, p.dout, p.dout + qelems, t0, nr, H, head, wave, lane);
+      stage_tile(b + 2 * TILE, p.qt16, p.qt16 + qelems, t0, nr, H, head, wave, lane);
+      if (wave < 2) {
+        const float* src = wave == 0 ? lse_h : del_h;
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), (short)0, Lq * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(vec0 + buf * 2 * BR + wave * BR), 4,
+                                                 (uint32_t)(min(j * BR + lane, Lq - 1) * 4), 0, 0, 0);
       }
-      wait_vm_all();
-      __syncthreads();
+    };
+    stage(0, 0);
+    wait_vm_all();
+    __syncthreads();
 
-      // S and dP: lane (g, n16) holds key n16 of the wave, queries 16qt + 4g + i
-      v4f s[4], dp[4];
+    for (int j = 0; j < nqb; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < nqb) stage(j + 1, buf ^ 1);  // the other buffer: last read in step j - 1
+      LDS uint8_t* tq = lds + buf * STAGE;  // Q (head_dim orientation), BF16
+      LDS uint8_t* tdo = tq + TILE;         // dO
+      LDS uint8_t* tqt = tq + 2 * TILE;     // Q (token orientation)
+      LDS float* vec = vec0 + buf * 2 * BR;
+
+      // S and dP: lane (g, n16) holds key 16t + n16 of the wave, queries 16qt + 4g + i. The
+      // fragments of query tile qt+1 are read while the matrix instructions of tile qt run; the
+      // four accumulation chains (S and dP of both key tiles) interleave.
+      v4f s[2][4], dp[2][4];
+      v8bf aq[2][4], ao[2][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        aq[0][u] = row_frag(tq, n16, 4 * u + g);
+        ao[0][u] = row_frag(tdo, n16, 4 * u + g);
+      }
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        v8bf aq[4], ao[4];
+        const int cur = qt & 1;
+        if (qt < 3) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          aq[u] = row_frag(tq, 16 * qt + n16, 4 * u + g);
-          ao[u] = row_frag(tdo, 16 * qt + n16, 4 * u + g);
-        }
-        s[qt] = dp[qt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s[qt] = mfma(aq[u], kf[u], s[qt]);
-          dp[qt] = mfma(ao[u], vf[u], dp[qt]);
+          for (int u = 0; u < 4; ++u) {
+            aq[cur ^ 1][u] = row_frag(tq, 16 * (qt + 1) + n16, 4 * u + g);
+            ao[cur ^ 1][u] = row_frag(tdo, 16 * (qt + 1) + n16, 4 * u + g);
+          }
         }
         group_end();
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            s[t][qt] = mfma(aq[cur][u], kf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][qt]);
+            dp[t][qt] = mfma(ao[cur][u], vf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : dp[t][qt]);
+          }
+        group_end();
       }
-      uint32_t pw[2][4], dw[2][4];
+      // the first group of dV/dK operands goes out before the softmax
+      v8bf bo[2][4], bq[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bo[0][i] = col_frag(tdo, 0, i, g, n16);
+        bq[0][i] = col_frag(tqt, 0, i, g, n16);
+      }
+      uint32_t pw[2][2][4], dw[2][2][4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        const v4f lv = *reinterpret_cast<LDS v4f*>(vec + 16 * qt + 4 * g);
+        const v4f ln = *reinterpret_cast<LDS v4f*>(vec + 16 * qt + 4 * g);
         const v4f dv4 = *reinterpret_cast<LDS v4f*>(vec + BR + 16 * qt + 4 * g);
-        float pr[4], ds[4];
+        float lv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(fmaf(s[qt][i], c, -lv[i]));
-          ds[i] = pr[i] * (dp[qt][i] - dv4[i]);
-        }
-        pw[qt >> 1][2 * (qt & 1)] = pk_bf16(pr[0], pr[1]);
-        pw[qt >> 1][2 * (qt & 1) + 1] = pk_bf16(pr[2], pr[3]);
-        dw[qt >> 1][2 * (qt & 1)] = pk_bf16(ds[0], ds[1]);
-        dw[qt >> 1][2 * (qt & 1) + 1] = pk_bf16(ds[2], ds[3]);
-      }
+        for (int i = 0; i < 4; ++i)  // LSE in log2 units; +inf past the sequence (P = 0 there)
+          lv[i] = j * BR + 16 * qt + 4 * g + i < Lq ? ln[i] * LOG2E : __builtin_inff();
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const v8bf ap = __builtin_bit_cast(v8bf, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
-        const v8bf ad = __builtin_bit_cast(v8bf, make_uint4(dw[st][0], dw[st][1], dw[st][2], dw[st][3]));
-#pragma unroll
-        for (int d0 = 0; d0 < 8; d0 += 4) {
-          v8bf bo[4], bq[4];
+        for (int t = 0; t < 2; ++t) {
+          float pr[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            bo[i] = col_frag(tdo, st, d0 + i, g, n16);
-            bq[i] = col_frag(tqt, st, d0 + i, g, n16);
+            pr[i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], c, -lv[i]));
+            ds[i] = pr[i] * (dp[t][qt][i] - dv4[i]);
           }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dv[d0 + i] = mfma(ap, bo[i], dv[d0 + i]);
-            dk[d0 + i] = mfma(ad, bq[i], dk[d0 + i]);
-          }
-          group_end();
+          pw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(pr[0], pr[1]);
+          pw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(pr[2], pr[3]);
+          dw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(ds[0], ds[1]);
+          dw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(ds[2], ds[3]);
         }
       }
+      // dV += P^T dO, dK += dS^T Qt over 4 groups (32-query half st, d tiles d0..d0+3), the next
+      // group's transposed reads going out before the current group's matrix instructions
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int st = gi >> 1, d0 = 4 * (gi & 1), cur = gi & 1;
+        if (gi < 3) {
+          const int st1 = (gi + 1) >> 1, d1 = 4 * ((gi + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bo[cur ^ 1][i] = col_frag(tdo, st1, d1 + i, g, n16);
+            bq[cur ^ 1][i] = col_frag(tqt, st1, d1 + i, g, n16);
+          }
+        }
+        group_end();
+        v8bf ap[2], ad[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ap[t] = __builtin_bit_cast(v8bf, make_uint4(pw[t][st][0], pw[t][st][1], pw[t][st][2], pw[t][st][3]));
+          ad[t] = __builtin_bit_cast(v8bf, make_uint4(dw[t][st][0], dw[t][st][1], dw[t][st][2], dw[t][st][3]));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            dv[t][d0 + i] = mfma(ap[t], bo[cur][i], dv[t][d0 + i]);
+            dk[t][d0 + i] = mfma(ad[t], bq[cur][i], dk[t][d0 + i]);
+          }
+        group_end();
+      }
+      wait_vm_all();
       __syncthreads();
     }
   }
 
   LDS float* ep = reinterpret_cast<LDS float*>(lds);
+  const bool mx = p.mx_dkv != 0;
   acc_to_lds(ep, dv, 1.0f, wave, g, n16);
   __syncthreads();
-  emit_rows(ep, p.dv, p.dv_scale, p.mx_dkv != 0, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
+  emit_rows(ep, p.dv, p.dv_scale, mx, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
+  emit_rows(ep + 64 * 128, p.dv, p.dv_scale, mx, p.scaling_mode, kbase + k_loc + 64, srow_k + k_loc + 64, k_loc + 64, Lk,
+            H, head);
   __syncthreads();
   acc_to_lds(ep, dk, p.softmax_scale, wave, g, n16);
   __syncthreads();
-  emit_rows(ep, p.dk, p.dk_scale, p.mx_dkv != 0, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
+  emit_rows(ep, p.dk, p.dk_scale, mx, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
+  emit_rows(ep + 64 * 128, p.dk, p.dk_scale, mx, p.scaling_mode, kbase + k_loc + 64, srow_k + k_loc + 64, k_loc + 64, Lk,
+            H, head);
 }
 
 // ---- dQ
+// One workgroup = BO queries of one (sequence, head); wave w owns queries 32w + 16t + n (t = 0, 1)
+// and walks the keys 64 at a time, double-buffered like the dK/dV pass.
 
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
-  LDS uint8_t* lds = (LDS uint8_t*)smem;
-  LDS uint8_t* tk = lds;              // K (head_dim orientation), BF16
-  LDS uint8_t* tv = lds + TILE;       // V (head_dim orientation)
-  LDS uint8_t* tkt = lds + 2 * TILE;  // K (token orientation)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_dyn[];
+  LDS uint8_t* lds = (LDS uint8_t*)smem_dyn;
 
-  const int H = p.num_heads, head = blockIdx.y;
-  const int row0 = blockIdx.x * BR;  // row of Q's padded scale storage
+  const int H = p.num_heads;
+  int blk, head;
+  block_head((int)(p.rows_q / BO), H, blk, head);
+  const int row0 = blk * BO;  // row of Q's padded scale storage
   const int seq = find_seq(p.cu_scale_q, p.num_seqs, row0);
   const int srow_q = p.cu_scale_q[seq];
   const int q_loc = row0 - srow_q;
   const int qbase = p.cu_q[seq], Lq = p.cu_q[seq + 1] - qbase;
   const int kbase = p.cu_k[seq], Lk = p.cu_k[seq + 1] - kbase;
-  const int srow_k = p.cu_scale_k[seq];
   if (q_loc >= Lq) return;  // pad rows only: nothing to write
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  v4f dq[8];
+  v4f dq[2][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) dq[dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) dq[t][dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (Lk > 0) {
-    // this lane's query (B operand column n16 of the wave's 16): Q and dO fragments, k = d
-    const int qv = q_loc + 16 * wave + n16;
-    const int qr = min(qv, Lq - 1);
-    const int64_t tq_ = qbase + qr;
-    v8bf qf[4], of[4];
-    {
+    // this lane's queries (B operand column n16 of tile t): Q and dO fragments, k = d
+    v8bf qf[2][4], of[2][4];
+    float l2[2], dl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qv = q_loc + WR * wave + 16 * t + n16;
+      const int qr = min(qv, Lq - 1);
+      const int64_t tq_ = qbase + qr;
       const uint8_t* qp = p.q + (tq_ * H + head) * 128 + 8 * g;
       const uint8_t* qs = p.q_scale + ((int64_t)(srow_q + qr) * H + head) * 4;
       const uint16_t* op = p.dout + (tq_ * H + head) * 128 + 8 * g;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint2 w = *reinterpret_cast<const uint2*>(qp + 32 * u);
-        qf[u] = __builtin_bit_cast(v8bf, fp8x8_bf16(w.x, w.y, e8m0_f(qs[u])));
-        of[u] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(op + 32 * u));
+        qf[t][u] = __builtin_bit_cast(v8bf, fp8x8_bf16(w.x, w.y, e8m0_f(qs[u])));
+        of[t][u] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(op + 32 * u));
       }
+      l2[t] = qv < Lq ? p.lse[(int64_t)head * p.total_q + tq_] * LOG2E : __builtin_inff();
+      dl[t] = p.delta[(int64_t)head * p.total_q + tq_];
     }
-    const float l2 = qv < Lq ? p.lse[(int64_t)head * p.total_q + tq_] * LOG2E : __builtin_inff();
-    const float dl = p.delta[(int64_t)head * p.total_q + tq_];
     const float c = p.softmax_scale * LOG2E;
     const int nkb = (Lk + BR - 1) / BR;
-
     const int64_t kelems = p.total_k * H * 128;
-    for (int j = 0; j < nkb; ++j) {
+
+    auto stage = [&](int j, int buf) {
       const int64_t t0 = kbase + (int64_t)j * BR;
       const int nr = Lk - j * BR;
-      stage_tile(tk, p.kd16, p.kd16 + kelems, t0, nr, H, head, wave, lane);
-      stage_tile(tv, p.vd16, p.vd16 + kelems, t0, nr, H, head, wave, lane);
-      stage_tile(tkt, p.kt16, p.kt16 + kelems, t0, nr, H, head, wave, lane);
-      wait_vm_all();
-      __syncthreads();
+      LDS uint8_t* b = lds + buf * STAGE;
+      stage_tile(b, p.kd16, p.kd16 + kelems, t0, nr, H, head, wave, lane);
+      stage_tile(b + TILE, p.vd16, p.vd16 + kelems, t0, nr, H, head, wave, lane);
+      stage_tile(b + 2 * TILE, p.kt16, p.kt16 + kelems, t0, nr, H, head, wave, lane);
+    };
+    stage(0, 0);
+    wait_vm_all();
+    __syncthreads();
 
-      // S^T and dP^T: lane (g, n16) holds query n16 of the wave, keys 16kt + 4g + i
-      v4f s[4], dp[4];
+    for (int j = 0; j < nkb; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < nkb) stage(j + 1, buf ^ 1);  // the other buffer: last read in step j - 1
+      LDS uint8_t* tk = lds + buf * STAGE;   // K (head_dim orientation), BF16
+      LDS uint8_t* tv = tk + TILE;           // V (head_dim orientation)
+      LDS uint8_t* tkt = tk + 2 * TILE;      // K (token orientation)
+      const int nr = Lk - j * BR;
+
+      // S^T and dP^T: lane (g, n16) holds query 16t + n16 of the wave, keys 16kt + 4g + i
+      // (pipelined like the dK/dV pass)
+      v4f s[2][4], dp[2][4];
+      v8bf ak[2][4], av[2][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ak[0][u] = row_frag(tk, n16, 4 * u + g);
+        av[0][u] = row_frag(tv, n16, 4 * u + g);
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        v8bf ak[4], av[4];
+        const int cur = kt & 1;
+        if (kt < 3) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ak[u] = row_frag(tk, 16 * kt + n16, 4 * u + g);
-          av[u] = row_frag(tv, 16 * kt + n16, 4 * u + g);
-        }
-        s[kt] = dp[kt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s[kt] = mfma(ak[u], qf[u], s[kt]);
-          dp[kt] = mfma(av[u], of[u], dp[kt]);
+          for (int u = 0; u < 4; ++u) {
+            ak[cur ^ 1][u] = row_frag(tk, 16 * (kt + 1) + n16, 4 * u + g);
+            av[cur ^ 1][u] = row_frag(tv, 16 * (kt + 1) + n16, 4 * u + g);
+          }
         }
         group_end();
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            s[t][kt] = mfma(ak[cur][u], qf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][kt]);
+            dp[t][kt] = mfma(av[cur][u], of[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : dp[t][kt]);
+          }
+        group_end();
       }
-      uint32_t dw[2][4];
+      v8bf bk[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bk[0][i] = col_frag(tkt, 0, i, g, n16);
+      uint32_t dw[2][2][4];
       auto scores_to_ds = [&](auto masked) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          float ds[4];
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -l2));
-            if constexpr (decltype(masked)::value) pr = 16 * kt + 4 * g + i < nr ? pr : 0.0f;
-            ds[i] = pr * (dp[kt][i] - dl);
+          for (int t = 0; t < 2; ++t) {
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float pr = __builtin_amdgcn_exp2f(fmaf(s[t][kt][i], c, -l2[t]));
+              if constexpr (decltype(masked)::value) pr = 16 * kt + 4 * g + i < nr ? pr : 0.0f;
+              ds[i] = pr * (dp[t][kt][i] - dl[t]);
+            }
+            dw[t][kt >> 1][2 * (kt & 1)] = pk_bf16(ds[0], ds[1]);
+            dw[t][kt >> 1][2 * (kt & 1) + 1] = pk_bf16(ds[2], ds[3]);
           }
-          dw[kt >> 1][2 * (kt & 1)] = pk_bf16(ds[0], ds[1]);
-          dw[kt >> 1][2 * (kt & 1) + 1] = pk_bf16(ds[2], ds[3]);
-        }
       };
       if (nr >= BR) scores_to_ds(std::false_type{});  // a full block: no key mask
       else scores_to_ds(std::true_type{});
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const v8bf ad = __builtin_bit_cast(v8bf, make_uint4(dw[st][0], dw[st][1], dw[st][2], dw[st][3]));
+      for (int gi = 0; gi < 4; ++gi) {
+        const int st = gi >> 1, d0 = 4 * (gi & 1), cur = gi & 1;
+        if (gi < 3) {
+          const int st1 = (gi + 1) >> 1, d1 = 4 * ((gi + 1) & 1);
 #pragma unroll
-        for (int d0 = 0; d0 < 8; d0 += 4) {
-          v8bf bk[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bk[i] = col_frag(tkt, st, d0 + i, g, n16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dq[d0 + i] = mfma(ad, bk[i], dq[d0 + i]);
-          group_end();
+          for (int i = 0; i < 4; ++i) bk[cur ^ 1][i] = col_frag(tkt, st1, d1 + i, g, n16);
         }
+        group_end();
+        v8bf ad[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          ad[t] = __builtin_bit_cast(v8bf, make_uint4(dw[t][st][0], dw[t][st][1], dw[t][st][2], dw[t][st][3]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) dq[t][d0 + i] = mfma(ad[t], bk[cur][i], dq[t][d0 + i]);
+        group_end();
       }
+      wait_vm_all();
       __syncthreads();
     }
   }
@@ -519,7 +641,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   LDS float* ep = reinterpret_cast<LDS float*>(lds);
   acc_to_lds(ep, dq, p.softmax_scale, wave, g, n16);
   __syncthreads();
-  emit_rows(ep, reinterpret_cast<uint8_t*>(p.dq), nullptr, false, 0, qbase + q_loc, 0, q_loc, Lq, H, head);
+  uint8_t* dqb = reinterpret_cast<uint8_t*>(p.dq);
+  emit_rows(ep, dqb, nullptr, false, 0, qbase + q_loc, 0, q_loc, Lq, H, head);
+  emit_rows(ep + 64 * 128, dqb, nullptr, false, 0, qbase + q_loc + 64, 0, q_loc + 64, Lq, H, head);
 }
 
 }  // namespace
@@ -531,10 +655,25 @@ hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s) {
   if (p.rows_q > 0 && p.rows_k > 0)
     hipLaunchKernelGGL(bwd_dequant_kernel, dim3((unsigned)((jobs_rows * p.num_heads * 16 + 255) / 256), 6), dim3(256), 0,
                        s, p);
+  // more than the default 64 KB of dynamic LDS: a per-kernel, per-device attribute, set once per device
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured.fetch_or(bit, std::memory_order_acq_rel);
+  }
   if (p.rows_k > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.rows_k / BR), (unsigned)p.num_heads), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.rows_k / BO * p.num_heads)), dim3(256), LDS_BYTES, s, p);
   if (p.rows_q > 0)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.rows_q / BR), (unsigned)p.num_heads), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.rows_q / BO * p.num_heads)), dim3(256), LDS_BYTES, s, p);
   return hipGetLastError();
 }
 
