@@ -465,10 +465,11 @@ def graph_ms_per_call(torch, call, per_graph=25, replays=20):
 
 
 def kernel_source_hash() -> str:
+    """sha256[:16] over the attention kernel's source and the headers it is compiled with."""
     import hashlib
     h = hashlib.sha256()
-    src = os.path.join(ROOT, "precision_attention_mxfp8_amd", "csrc", "attn_fwd.hip")
-    h.update(open(src, "rb").read())
+    for name in ("attn_fwd.hip", "device_common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "precision_attention_mxfp8_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
