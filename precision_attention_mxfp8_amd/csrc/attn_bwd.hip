@@ -197,10 +197,10 @@ __device__ __forceinline__ void delta_rows(const BwdParams& p, int64_t gid) {
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-  if (in && sub == 0) {
+  if (in && sub == 0) {  // stored negated: -D is the initial value of the dP accumulators
     const int64_t tok = row / p.num_heads;
     const int head = (int)(row - tok * p.num_heads);
-    p.delta[(int64_t)head * p.total_q + tok] = acc;
+    p.delta[(int64_t)head * p.total_q + tok] = -acc;
   }
 }
 
@@ -384,8 +384,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       // S and dP: lane (g, n16) holds key 16t + n16 of the wave, queries 16qt + 4g + i. The
       // fragments of query tile qt+1 are read while the matrix instructions of tile qt run; the
       // four accumulation chains (S and dP of both key tiles) interleave.
-      v4f s[2][4], dp[2][4];
+      // dP starts from -D of its row, so that it ends as dP - D (the workspace holds -D)
+      v4f s[2][4], dp[2][4], nd[4];
       v8bf aq[2][4], ao[2][4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) nd[qt] = *reinterpret_cast<LDS v4f*>(vec + BR + 16 * qt + 4 * g);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         aq[0][u] = row_frag(tq, n16, 4 * u + g);
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             s[t][qt] = mfma(aq[cur][u], kf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][qt]);
-            dp[t][qt] = mfma(ao[cur][u], vf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : dp[t][qt]);
+            dp[t][qt] = mfma(ao[cur][u], vf[t][u], u == 0 ? nd[qt] : dp[t][qt]);
           }
         group_end();
       }
@@ -419,28 +422,34 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         bq[0][i] = col_frag(tqt, 0, i, g, n16);
       }
       uint32_t pw[2][2][4], dw[2][2][4];
+      // LSE in log2 units; on the sequence's last step, +inf past its end (P = 0 there)
+      auto probs = [&](auto tail) {
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const v4f ln = *reinterpret_cast<LDS v4f*>(vec + 16 * qt + 4 * g);
-        const v4f dv4 = *reinterpret_cast<LDS v4f*>(vec + BR + 16 * qt + 4 * g);
-        float lv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)  // LSE in log2 units; +inf past the sequence (P = 0 there)
-          lv[i] = j * BR + 16 * qt + 4 * g + i < Lq ? ln[i] * LOG2E : __builtin_inff();
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float pr[4], ds[4];
+        for (int qt = 0; qt < 4; ++qt) {
+          const v4f ln = *reinterpret_cast<LDS v4f*>(vec + 16 * qt + 4 * g);
+          float lv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            pr[i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], c, -lv[i]));
-            ds[i] = pr[i] * (dp[t][qt][i] - dv4[i]);
+            lv[i] = ln[i] * LOG2E;
+            if constexpr (decltype(tail)::value) lv[i] = j * BR + 16 * qt + 4 * g + i < Lq ? lv[i] : __builtin_inff();
           }
-          pw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(pr[0], pr[1]);
-          pw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(pr[2], pr[3]);
-          dw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(ds[0], ds[1]);
-          dw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(ds[2], ds[3]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float pr[4], ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pr[i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], c, -lv[i]));
+              ds[i] = pr[i] * dp[t][qt][i];
+            }
+            pw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(pr[0], pr[1]);
+            pw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(pr[2], pr[3]);
+            dw[t][qt >> 1][2 * (qt & 1)] = pk_bf16(ds[0], ds[1]);
+            dw[t][qt >> 1][2 * (qt & 1) + 1] = pk_bf16(ds[2], ds[3]);
+          }
         }
-      }
+      };
+      if (j * BR + BR <= Lq) probs(std::false_type{});
+      else probs(std::true_type{});
       // dV += P^T dO, dK += dS^T Qt over 4 groups (32-query half st, d tiles d0..d0+3), the next
       // group's transposed reads going out before the current group's matrix instructions
 #pragma unroll
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
         of[t][u] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(op + 32 * u));
       }
       l2[t] = qv < Lq ? p.lse[(int64_t)head * p.total_q + tq_] * LOG2E : __builtin_inff();
-      dl[t] = p.delta[(int64_t)head * p.total_q + tq_];
+      dl[t] = p.delta[(int64_t)head * p.total_q + tq_];  // -D
     }
     const float c = p.softmax_scale * LOG2E;
     const int nkb = (Lk + BR - 1) / BR;
@@ -588,7 +597,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             s[t][kt] = mfma(ak[cur][u], qf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][kt]);
-            dp[t][kt] = mfma(av[cur][u], of[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : dp[t][kt]);
+            dp[t][kt] = mfma(av[cur][u], of[t][u], u == 0 ? v4f{dl[t], dl[t], dl[t], dl[t]} : dp[t][kt]);
           }
         group_end();
       }
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
             for (int i = 0; i < 4; ++i) {
               float pr = __builtin_amdgcn_exp2f(fmaf(s[t][kt][i], c, -l2[t]));
               if constexpr (decltype(masked)::value) pr = 16 * kt + 4 * g + i < nr ? pr : 0.0f;
-              ds[i] = pr * (dp[t][kt][i] - dl[t]);
+              ds[i] = pr * dp[t][kt][i];  // dP - D
             }
             dw[t][kt >> 1][2 * (kt & 1)] = pk_bf16(ds[0], ds[1]);
             dw[t][kt >> 1][2 * (kt & 1) + 1] = pk_bf16(ds[2], ds[3]);

@@ -85,7 +85,7 @@ struct BwdParams {
   const int32_t* cu_k;
   const int32_t* cu_scale_q;
   const int32_t* cu_scale_k;
-  float* delta;  // (H, total_q), in the workspace
+  float* delta;  // -D = -rowsum(dO * O), (H, total_q), in the workspace
   // BF16 copies in the workspace (tokens, H, 128): Q and K in both orientations, V along head_dim
   uint16_t* qd16;
   uint16_t* qt16;
