@@ -4,7 +4,10 @@ A step is one pass of the whole path over one batch of synthetic input already r
 HBM: MXFP8-quantize Q and K (RCEIL), cast V to E4M3 (fp8 PV mode), and the fused attention
 forward. The three preparation passes share one launch (prepare_qkv; --separate-prep launches
 them one by one). The per-tensor workload casts Q, K (with K's group maxima, the precision
-guard's bound on |k|) and V instead. The packed-sequence metadata is built once, before timing.
+guard's bound on |k|) and V instead. With BF16 V (--pv-mode bf16) the K quantizer also writes K's
+quantized values as BF16 (2 B per element more), which the attention's tiles that fail the
+precision guard load instead of converting K themselves (--no-k-deq: without). The packed-sequence
+metadata is built once, before timing.
 
 Prints ONE JSON line:
 * value = attention FLOPs (4 * Lq * Lk * H * D summed over sequences) per second of whole step,
@@ -81,6 +84,8 @@ def parse():
                     help="measurement window of the README protocol pass (seconds)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other PV modes, the BF16 forward, the backward and the peak loops")
+    ap.add_argument("--no-k-deq", action="store_true",
+                    help="bf16 PV: quantize K without its BF16 values (guard-failing tiles then convert K themselves)")
     ap.add_argument("--separate-prep", action="store_true",
                     help="launch the Q, K quantizers and the V cast separately instead of as one kernel")
     ap.add_argument("--b2b-iters", type=int, default=0,
@@ -123,6 +128,7 @@ def main():
     # every output (quantized operands, O, LSE) is allocated once; each step writes into it
     h = wl.num_heads
     kgm = None
+    kdeq = None
     if per_tensor:
         qx = torch.empty((mq.total_tokens, h, 128), dtype=torch.uint8, device=dev)
         kx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev)
@@ -130,9 +136,13 @@ def main():
     else:
         qx = lp.Mxfp8Tensor(torch.empty((mq.total_tokens, h, 128), dtype=torch.uint8, device=dev),
                             torch.empty((mq.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mq)
+        # with BF16 V the K quantizer also writes K's quantized values as BF16, which the kernel's
+        # guard-failing tiles load instead of converting every K block themselves
+        kdeq = (torch.empty((mk.total_tokens, h, 128), dtype=torch.bfloat16, device=dev)
+                if pv_mode == "bf16" and not args.no_k_deq else None)
         kx = lp.Mxfp8Tensor(torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev),
                             torch.empty((mk.total_scale_rows, h, 4), dtype=torch.uint8, device=dev), mk,
-                            torch.empty((mk.total_scale_rows // 16, h), dtype=torch.uint8, device=dev))
+                            torch.empty((mk.total_scale_rows // 16, h), dtype=torch.uint8, device=dev), kdeq)
     vx = torch.empty((mk.total_tokens, h, 128), dtype=torch.uint8, device=dev) if pv_mode == "fp8" else v
     plan = lp.AttnPlan(mq, mk, h, pv_mode=pv_mode, mx=not per_tensor, tile_order=order)
     out, lse = plan.out, plan.lse
@@ -284,7 +294,9 @@ def main():
                    "cu_scale_k": list(mk.cu_scale_host) if not per_tensor else None,
                    "heads": wl.num_heads, "head_dim": 128, "seed": args.seed,
                    "step": ("quantize Q,K + cast V (one launch) + attention forward" if fused_prep else
-                            "quantize Q,K + cast V + attention forward") if not per_tensor
+                            "quantize Q,K + cast V + attention forward" if pv_mode == "fp8" else
+                            "quantize Q, K (with K's BF16 values) + attention forward" if kdeq is not None else
+                            "quantize Q, K + attention forward") if not per_tensor
                    else "cast Q, K (with group maxima), V + attention forward"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LPFA_ABI_VERSION 8
+#define LPFA_ABI_VERSION 9
 
 #define LPFA_OK 0
 #define LPFA_EIO (-5)      /* kernel launch failed */
@@ -104,6 +104,13 @@ const char* lpfa_last_error(void);
  *                k (rows 16k .. 16k+15) that are not pad rows, 0 if all of them are. Passed to
  *                lp_attn_varlen_fwd as k_scale_group_max for K, it replaces the attention
  *                kernel's scan of the K scales (same results).
+ *   deq          optional output (NULL: not written) BF16 (T, num_heads, 128), contiguous,
+ *                16-byte aligned: the quantized values themselves, payload * 2^e, converted to
+ *                BF16 exactly as the attention's guarded path converts them (one E4M3 code
+ *                times a power of two has at most 4 significant bits). Passed to
+ *                lp_attn_varlen_fwd as k_deq for K, it spares the tiles that fail the precision
+ *                guard their own conversion of every K block (same results). 2 bytes per element
+ *                more; a design choice for gfx950, whose FP8 accumulation needs the guard.
  * Errors: LPFA_EINVAL for NULL pointers (unless the tensor is empty), negative sizes,
  * misalignment, bad enum values; LPFA_ENOTSUP for head_dim != 128.
  */
@@ -111,7 +118,7 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
                           int64_t total_tokens, int32_t num_heads, int32_t head_dim,
                           const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
                           int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
-                          uint8_t* scales, uint8_t* group_max, void* stream);
+                          uint8_t* scales, uint8_t* group_max, uint16_t* deq, void* stream);
 
 /*
  * mxfp8_quantize_varlen_tokens - MXFP8 quantization along tokens (the P V operand's V).
@@ -324,6 +331,13 @@ typedef struct lpfa_attn_args {
    * 0.0137 * fp8_score_guard in log2 units (random-sign data by far less). 0 selects
    * LPFA_FP8_SCORE_GUARD_DEFAULT; a negative value never takes FP8 scores; NaN is LPFA_EINVAL. */
   float fp8_score_guard;
+
+  /* Optional (ABI 9; NULL: none): K's quantized values as BF16, (total_k, num_heads, 128)
+   * contiguous and 16-byte aligned, as mxfp8_quantize_varlen writes them into its deq output.
+   * Tiles that fail the precision guard then load their K blocks from it instead of converting
+   * every block of the payload themselves; results are identical either way. MX mode (q_scale
+   * and k_scale set) with pv_mode LPFA_PV_BF16 only, else LPFA_EINVAL. */
+  const void* k_deq;
 } lpfa_attn_args;
 
 /*

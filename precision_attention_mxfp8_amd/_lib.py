@@ -20,7 +20,7 @@ DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 SCALING = {"rceil": 0, "floor": 1}
 PV_MODES = {"bf16": 0, "fp8": 1, "mx": 2}
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 EXPORTS = ("lpfa_abi_version", "lpfa_last_error", "mxfp8_quantize_varlen", "mxfp8_quantize_varlen_tokens",
            "mxfp8_prepare_qkv", "lp_fp8_cast_e4m3", "lp_fp8_cast_current", "lp_fp8_cast_current_noalloc", "lp_attn_varlen_fwd",
@@ -61,6 +61,7 @@ class AttnArgs(ctypes.Structure):
         ("v_scale", _p),
         ("qk_bf16", _i32),
         ("fp8_score_guard", ctypes.c_float),
+        ("k_deq", ctypes.c_void_p),
     ]
 
 
@@ -117,7 +118,7 @@ def load() -> ctypes.CDLL:
         lib.lpfa_last_error.argtypes = []
         lib.mxfp8_quantize_varlen.restype = ctypes.c_int
         lib.mxfp8_quantize_varlen.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
-                                              _i32, _i64, ctypes.c_int, _p, _p, _p, _p]
+                                              _i32, _i64, ctypes.c_int, _p, _p, _p, _p, _p]
         lib.mxfp8_quantize_varlen_tokens.restype = ctypes.c_int
         lib.mxfp8_quantize_varlen_tokens.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _p, _p,
                                                      _i32, _i64, ctypes.c_int, _p, _p, _p]

@@ -91,12 +91,16 @@ class Mxfp8Tensor:
 
     ``group_max`` (optional, (sum P(L_i) / 16, H) uint8): the largest scale byte of each 16-row
     group of the scale storage over its real rows (0 for a group of pad rows only), written by the
-    quantizer. Used for K by the attention's precision guard (results are the same without it)."""
+    quantizer. Used for K by the attention's precision guard (results are the same without it).
+    ``deq`` (optional, (T, H, 128) BF16): the quantized values themselves (payload times the block
+    scale), written by the quantizer on request (``with_deq``). Used for K by the BF16-V forward's
+    tiles that fail the precision guard (results are the same without it)."""
 
     payload: torch.Tensor
     scales: torch.Tensor
     meta: VarlenMeta
     group_max: Optional[torch.Tensor] = None
+    deq: Optional[torch.Tensor] = None
 
 
 @dataclass
@@ -134,10 +138,12 @@ def _check_out(t: torch.Tensor, shape, dtype, device, name: str) -> None:
 
 
 def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str = "rceil",
-                          out: Optional[Mxfp8Tensor] = None) -> Mxfp8Tensor:
+                          out: Optional[Mxfp8Tensor] = None, with_deq: bool = False) -> Mxfp8Tensor:
     """MXFP8-quantize packed (tokens, heads, 128) BF16/FP32 ``x`` (RCEIL default, FLOOR optional).
 
-    ``out``: an Mxfp8Tensor of the right shapes to write into (reused buffers); a new one otherwise.
+    ``out``: an Mxfp8Tensor of the right shapes to write into (reused buffers); a new one otherwise
+    (its ``deq``, if set, is written too). ``with_deq``: a new tensor also carries ``deq``, the
+    quantized values as BF16 (for K of the BF16-V forward on data that fails the precision guard).
     """
     mode = _lib.SCALING.get(scaling_mode)
     if mode is None:
@@ -151,18 +157,21 @@ def quantize_mxfp8_varlen(x: torch.Tensor, meta: VarlenMeta, scaling_mode: str =
         payload = torch.empty((t, h, HEAD_DIM), dtype=torch.uint8, device=x.device)
         scales = torch.empty((meta.total_scale_rows, h, 4), dtype=torch.uint8, device=x.device)
         group_max = torch.empty(gshape, dtype=torch.uint8, device=x.device)
-        out = Mxfp8Tensor(payload, scales, meta, group_max)
+        deq = torch.empty((t, h, HEAD_DIM), dtype=torch.bfloat16, device=x.device) if with_deq else None
+        out = Mxfp8Tensor(payload, scales, meta, group_max, deq)
     else:
         _check_out(out.payload, (t, h, HEAD_DIM), torch.uint8, x.device, "out.payload")
         _check_out(out.scales, (meta.total_scale_rows, h, 4), torch.uint8, x.device, "out.scales")
         if out.group_max is not None:
             _check_out(out.group_max, gshape, torch.uint8, x.device, "out.group_max")
+        if out.deq is not None:
+            _check_out(out.deq, (t, h, HEAD_DIM), torch.bfloat16, x.device, "out.deq")
         if out.meta is not meta:
-            out = Mxfp8Tensor(out.payload, out.scales, meta, out.group_max)
+            out = Mxfp8Tensor(out.payload, out.scales, meta, out.group_max, out.deq)
     rc = _lib.load().mxfp8_quantize_varlen(
         x.data_ptr(), dt, x.stride(0), x.stride(1), t, h, HEAD_DIM, meta.cu_seqlens.data_ptr(),
         meta.cu_scale.data_ptr(), meta.num_seqs, meta.total_scale_rows, mode, out.payload.data_ptr(),
-        out.scales.data_ptr(), None if out.group_max is None else out.group_max.data_ptr(), _stream())
+        out.scales.data_ptr(), _ptr(out.group_max), _ptr(out.deq), _stream())
     if rc:
         _lib.check("mxfp8_quantize_varlen", rc)
     return out
@@ -471,6 +480,12 @@ class AttnPlan:
                 a.k_scale_group_max = gm.data_ptr()
             else:
                 a.k_scale_group_max = None
+            # K's BF16 values (from the quantizer) serve the BF16-V kernel's guard-failing tiles
+            if k.deq is not None and self.pv_mode == "bf16":
+                _check_out(k.deq, (self.meta_k.total_tokens, self.num_heads, HEAD_DIM), torch.bfloat16, self._dev, "k.deq")
+                a.k_deq = k.deq.data_ptr()
+            else:
+                a.k_deq = None
             _check_out(q.scales, (self.meta_q.total_scale_rows, self.num_heads, 4), torch.uint8, self._dev, "q.scales")
             _check_out(k.scales, (self.meta_k.total_scale_rows, self.num_heads, 4), torch.uint8, self._dev, "k.scales")
         else:

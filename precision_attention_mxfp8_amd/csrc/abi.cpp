@@ -52,11 +52,15 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
                           int64_t total_tokens, int32_t num_heads, int32_t head_dim,
                           const int32_t* cu_seqlens, const int32_t* cu_scale, int32_t num_seqs,
                           int64_t total_scale_rows, int scaling_mode, uint8_t* payload,
-                          uint8_t* scales, uint8_t* group_max, void* stream) {
+                          uint8_t* scales, uint8_t* group_max, uint16_t* deq, void* stream) {
   if (int rc = lpfa::check_quantize(x, x_dtype, stride_tok, stride_head, total_tokens, num_heads,
                                     head_dim, cu_seqlens, cu_scale, num_seqs, total_scale_rows,
                                     scaling_mode, payload, scales))
     return rc;
+  if (deq != nullptr && (reinterpret_cast<uintptr_t>(deq) & 15u)) {
+    lpfa::set_error("deq is not 16-byte aligned");
+    return LPFA_EINVAL;
+  }
   lpfa::QuantParams p{};
   p.x = x;
   p.x_dtype = x_dtype;
@@ -71,6 +75,7 @@ int mxfp8_quantize_varlen(const void* x, int x_dtype, int64_t stride_tok, int64_
   p.payload = payload;
   p.scales = scales;
   p.group_max = group_max;
+  p.deq = deq;
   return launch_status(lpfa::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize");
 }
 
@@ -267,6 +272,8 @@ int lp_attn_varlen_fwd(const lpfa_attn_args* a, void* stream) {
     p.qk_bf16 = a->qk_bf16;
     p.guard = a->fp8_score_guard == 0.0f ? LPFA_FP8_SCORE_GUARD_DEFAULT : a->fp8_score_guard;
     p.v_end = static_cast<const uint8_t*>(a->v) + vspan;
+    p.k_deq = static_cast<const uint8_t*>(a->k_deq);
+    p.k_deq_end = p.k_deq ? p.k_deq + a->total_k * a->num_heads * 256 : nullptr;
   }
   p.total_q = a->total_q;
   p.num_heads = a->num_heads;

@@ -211,10 +211,11 @@ struct PFrag<false> { uint32_t w[4][2][4]; };
 // path of the BF16-V kernel: MX Q and K dequantized exactly to BF16 (Q once per tile into
 // registers, K once per block into BF16 LDS tiles), then the BF16 pipeline below. QB: Q and K are
 // BF16 (the BF16 FlashAttention forward: BF16 scores and BF16 P V, one wave group).
-template <bool MX, bool FP8V, bool VMX, bool QB = false, bool DQ = false>
+template <bool MX, bool FP8V, bool VMX, bool QB = false, bool DQ = false, bool DQS = false>
 struct Attn {
   static_assert(!QB || (!MX && !FP8V && !VMX), "BF16 Q/K come with BF16 V only");
   static_assert(!DQ || (MX && !FP8V && !VMX && !QB), "the dequantized path is the BF16-V kernel's");
+  static_assert(!DQS || DQ, "K's BF16 values from the quantizer serve the DQ pipeline");
   static constexpr bool KB16 = QB || DQ;  // K in LDS and Q in registers are BF16
   using L = Lay<FP8V, KB16>;
   using PF = PFrag<FP8V>;
@@ -231,7 +232,8 @@ struct Attn {
   int scq, sck;              // its first scale rows (MX mode)
   int lane, wave, n16, g;    // wave: index inside the group (queries 32*wave ..)
   int grp, ng;               // wave group, and the number of key blocks it processes
-  const uint8_t* kbase;      // key row 0 of this (sequence, head)
+  const uint8_t* kbase;      // key row 0 of this (sequence, head) (DQS: of K's BF16 values)
+  const uint8_t* kend;       // one past the last byte of that tensor
   const uint8_t* vbase;      // value row 0 (bytes)
   int64_t k_st_b, v_st_b;    // row strides in bytes
   const uint8_t* ksc_base;   // scale word of key row 0 of this (sequence, head)
@@ -323,13 +325,13 @@ struct Attn {
   __device__ __forceinline__ void dma_k(int tg, int b, int buf) {
     uint8_t* area = lds + (tg - grp) * L::GROUP_BYTES;
     LDS uint8_t* dst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 4 * wave * 1024);
-    if constexpr (QB) {
+    if constexpr (QB || DQS) {
       // BF16 rows of 256 bytes: instruction i of wave w fills region 8w + i = rows 32w + 4i ..
       // 32w + 4i + 3; lane L fills row 32w + 4i + L/16, LDS chunk L%16, with the row's chunk
       // (L%16) ^ (row%16) (the score reads then hit 16 different banks for 16 rows)
       LDS uint8_t* qdst = LDS_PTR(uint8_t, area + L::OFF_K + buf * L::K_BYTES + 8 * wave * 1024);
       const int r16 = lane >> 4;
-      const auto r = rsrc(kbase + (int64_t)(b * BN + 32 * wave) * k_st_b, p.k_end);
+      const auto r = rsrc(kbase + (int64_t)(b * BN + 32 * wave) * k_st_b, kend);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = 4 * i + r16;  // (32w + row) % 16 == row % 16
@@ -948,7 +950,7 @@ struct Attn {
   // PAR = j % 2 (a constant: the V buffers are chosen at compile time).
   template <bool FAST, bool FIRST, bool LAST, int PAR>
   __device__ __forceinline__ void iteration1(int j, v4f s[8][2], const PF& pf_prev, PF& pf_cur) {
-    if constexpr (DQ) {
+    if constexpr (DQ && !DQS) {
       if (j + 2 < ng) dq_load_k(blk(j + 2));
     } else {
       if (j + 2 < ng) dma_k(0, blk(j + 2), j & 1);
@@ -956,7 +958,7 @@ struct Attn {
     dma_v(PAR, blk(j), 0);
     step<FAST && !LAST, !FIRST, LAST, PAR>(j, s, pf_prev, pf_cur);
     if (!FAST && !LAST) scores_bf16((j + 1) & 1, s);
-    if constexpr (DQ) {  // block j+2's K, staged in registers during the step, into K buffer j % 2
+    if constexpr (DQ && !DQS) {  // block j+2's K, staged in registers during the step, into K buffer j % 2
       if (j + 2 < ng) dq_store_k(j & 1);
     }
     wait_vm_all();
@@ -1147,8 +1149,16 @@ struct Attn {
   // the DQ pipeline for the BF16-V kernel), which always completes and returns true.
   template <int MODE>
   __device__ __forceinline__ bool run(int qtile) {
-    constexpr bool GUARD = MODE != 1 && !KB16;  // this call evaluates the guard (BF16 scores need none)
+    // MODE 3 (DQS only): the DQ pipeline started on speculation; it evaluates the guard in its
+    // prologue, from loads it makes anyway, and returns false (no load in flight) if the tile may
+    // take FP8 scores after all.
+    static_assert(MODE != 3 || DQS, "speculative start: the DQ pipeline with K's BF16 values");
+    constexpr bool GUARD = (MODE != 1 && !KB16) || MODE == 3;  // this call evaluates the guard
     constexpr bool MAY_SLOW = MODE != 0;  // this call may run the BF16 score loop
+    // The one-group MX kernel decides before its first K and Q loads, from the Q scale words and
+    // the K bound alone: a tile that fails then leaves at once for the DQ pipeline instead of
+    // first loading and waiting for the FP8 path's operands.
+    constexpr bool EARLY = MODE == 0 && G == 1 && MX && !KB16;
     H = p.num_heads;
     qtile0 = qtile;
     const int q0 = qtile * BM;
@@ -1167,9 +1177,16 @@ struct Attn {
     const float kd = p.k_descale ? p.k_descale[seq * p.kd_ss + head * p.kd_sh] : 1.0f;
     c = (p.scale_log2 * qd) * kd;  // identical arithmetic with or without descales
 
-    kbase = p.k + ((int64_t)k_start * p.k_st + (int64_t)head * p.k_sh) * (QB ? 2 : 1);
+    if constexpr (DQS) {  // K's quantized values as BF16: (total_k, H, 128) contiguous
+      kbase = p.k_deq + ((int64_t)k_start * H + head) * 256;
+      k_st_b = (int64_t)H * 256;
+      kend = p.k_deq_end;
+    } else {
+      kbase = p.k + ((int64_t)k_start * p.k_st + (int64_t)head * p.k_sh) * (QB ? 2 : 1);
+      k_st_b = p.k_st * (QB ? 2 : 1);
+      kend = p.k_end;
+    }
     vbase = reinterpret_cast<const uint8_t*>(p.v) + ((int64_t)k_start * p.v_st + (int64_t)head * p.v_sh) * (FP8V ? 1 : 2);
-    k_st_b = p.k_st * (QB ? 2 : 1);
     v_st_b = p.v_st * (FP8V ? 1 : 2);
     ksc_base = MX ? p.k_scale + ((int64_t)sck * H + head) * 4 : nullptr;
     kgm_base = nullptr;
@@ -1183,9 +1200,30 @@ struct Attn {
       gcount = (k_start + Lk - 1) / 16 - g0 + 1;
     }
     if (GUARD && (MX || kgm_base != nullptr)) guard_prefetch();
+    if constexpr (EARLY) {
+      if (nb > 0) {
+        uint32_t qms = 0;  // largest scale byte of the tile's queries (byte g of each row's word)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int qi = q0 + wave * 32 + nt * 16 + n16;
+          const bool in = qi < Lq;
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)scq + (in ? qi : Lq - 1)) * H + head) * 4);
+          qms = max(qms, in ? (sw >> (8 * g)) & 0xFFu : 0u);
+        }
+        qbound = 448.0f * e8m0_to_float(wave_max_u32(qms));
+        float* red = reinterpret_cast<float*>(lds + L::OFF_RED);
+        guard_publish(red);
+        wait_vm_all();
+        __syncthreads();
+        if (!fp8_scores_ok_tile(red)) return false;  // uniform; no load in flight
+      }
+    }
 
     // start the first loads before touching Q
-    if constexpr (DQ) {
+    if constexpr (DQS) {
+      if (ng > 0) dma_k(0, blk(0), 0);
+      if (ng > 1) dma_k(0, blk(1), 1);
+    } else if constexpr (DQ) {
       if (ng > 0) dq_load_k(blk(0));  // stored as BF16 once Q's loads have gone out
     } else if (ng > 0) {
       if (grp == 0) {
@@ -1200,6 +1238,7 @@ struct Attn {
     // ---- Q fragments: BF16 in registers (QB; DQ: dequantized exactly), or FP8 (score B operand)
     // through LDS; the guarded path of the two-group kernel reloads FP8 Q as BF16 ----
     if constexpr (DQ) {
+      uint32_t qms = 0;  // MODE 3: largest scale byte of the tile's queries
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int qi = q0 + wave * 32 + nt * 16 + n16;
@@ -1207,6 +1246,7 @@ struct Attn {
         const int qc = in ? qi : Lq - 1;
         const uint8_t* qp = p.q + (int64_t)(q_start + qc) * p.q_st + (int64_t)head * p.q_sh;
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(p.q_scale + (((int64_t)scq + qc) * H + head) * 4);
+        if (MODE == 3) qms = max(qms, in ? (sw >> (8 * g)) & 0xFFu : 0u);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           uint2 w = ldg8(qp + 32 * u + 8 * g);  // head_dim 32u + 8g .. 32u + 8g + 7: scale block u
@@ -1214,7 +1254,8 @@ struct Attn {
           qb16[nt][u] = fp8x8_to_bf16(w.x, w.y, e8m0_to_float((sw >> (8 * u)) & 0xFFu));
         }
       }
-      if (ng > 0) {
+      if (MODE == 3) qbound = 448.0f * e8m0_to_float(wave_max_u32(qms));
+      if (!DQS && ng > 0) {
         dq_store_k(0);
         if (ng > 1) {
           dq_load_k(blk(1));
@@ -1276,7 +1317,7 @@ struct Attn {
         qa[nt * 128 + 64] = v4u_t{(unsigned)qf[nt][4], (unsigned)qf[nt][5], (unsigned)qf[nt][6], (unsigned)qf[nt][7]};
       }
     }
-    if (!GUARD) {
+    if (!GUARD || EARLY || KB16) {
     } else if (MX) {
       qbound = 448.0f * e8m0_to_float(wave_max_u32(qmax_scale));
     } else {
@@ -1295,15 +1336,18 @@ struct Attn {
 
     if (nb > 0) {
       float* red = reinterpret_cast<float*>(lds - grp * L::GROUP_BYTES + L::OFF_RED);
-      if (GUARD) guard_publish(red);
+      if (GUARD && !EARLY) guard_publish(red);
       wait_vm_all();
       __syncthreads();
       if constexpr (KB16) {
+        if constexpr (MODE == 3) {
+          if (fp8_scores_ok_tile(red)) return false;  // uniform; every load has landed
+        }
         main_loop<true>(niter);
       } else if constexpr (MODE == 1) {
         main_loop<false>(niter);
       } else if constexpr (MODE == 0) {
-        if (!fp8_scores_ok_tile(red)) return false;  // uniform: every wave reads the same slots
+        if (!EARLY && !fp8_scores_ok_tile(red)) return false;  // uniform: every wave reads the same slots
         main_loop<true>(niter);
       } else {
         if (fp8_scores_ok_tile(red)) main_loop<true>(niter); else main_loop<false>(niter);
@@ -1405,7 +1449,25 @@ __global__ __launch_bounds__(256 * Groups<FP8V>::G) void attn_fwd_kernel(AttnPar
   } else if constexpr (Groups<FP8V>::G == 1) {
     // BF16 V with MX Q/K: a tile that fails the guard runs the DQ pipeline (K dequantized once per
     // block into BF16 LDS tiles, Q into BF16 registers), inline: 512 registers hold both paths
-    if (!a.template run<0>(qtile)) {
+    if (p.k_deq != nullptr) {
+      // K's BF16 values come from the quantizer, a sign that the data is expected to fail the
+      // guard: the DQ pipeline (K loaded like BF16 K) starts at once and takes the decision in its
+      // prologue; a tile that may take FP8 scores then runs the FP8 path.
+      Attn<MX, false, false, false, true, true> d(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
+      d.seq = seq;
+      d.head = head;
+      d.load_meta();
+      if (!d.template run<3>(qtile)) {
+        __syncthreads();  // every wave has read the decision before the FP8 path's LDS writes
+        if (!a.template run<0>(qtile)) {  // the same bounds pass again: FP8 scores (kept total)
+          __syncthreads();
+          d.template run<1>(qtile);
+        }
+      }
+    } else if (!a.template run<0>(qtile)) {
+      // every wave has read the guard's decision before the BF16 K tiles (which cover the
+      // reduction slots) are written
+      __syncthreads();
       Attn<MX, false, false, false, true> d(p, smem, grp, LDS_PTR(uint8_t, va), LDS_PTR(uint8_t, vb));
       d.seq = seq;
       d.head = head;

@@ -45,6 +45,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(cvt_f32x2_t{a, b}, cvt_bf16x2_t));
 }
 
+// Four E4M3 codes (one word) times the power of two `scale` (only its exponent field is read, so
+// an E8M0 byte b converts as __uint_as_float(b << 23), b = 0 as 2^-127) -> four BF16 in two words,
+// with the hardware's scaled conversion. The quantizer's BF16 output of the quantized values and
+// the attention's dequantization of K both use it, so the two agree bit for bit.
+__device__ __forceinline__ uint2 fp8x4_scaled_bf16(uint32_t w, float scale) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, scale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, scale, true)));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -20,6 +20,7 @@ struct QuantParams {
   uint8_t* payload;
   uint8_t* scales;
   uint8_t* group_max;  // optional: largest scale byte of each (16-row group, head)
+  uint16_t* deq;       // optional: the quantized values as BF16, (T, H, 128) contiguous
 };
 
 struct CastParams {
@@ -64,6 +65,8 @@ struct AttnParams {
   float scale_log2;   // softmax_scale * log2(e)
   int32_t qk_bf16;    // Q and K are BF16 (the BF16 FlashAttention forward)
   float guard;        // FP8 scores when c * max|q| * max|k| <= guard (negative: never)
+  const uint8_t* k_deq;      // optional: K's quantized values as BF16, (total_k, H, 128) contiguous
+  const uint8_t* k_deq_end;  // one past its last byte
 };
 
 // Attention backward (lp_attn_varlen_bwd); every tensor contiguous, (tokens, heads, 128).

@@ -94,6 +94,11 @@ __device__ __forceinline__ void quantize_group(const QuantParams& p, unsigned bi
     uint32_t w0 = cvt4_e4m3(clamp448(v[0] * inv), clamp448(v[1] * inv), clamp448(v[2] * inv), clamp448(v[3] * inv));
     uint32_t w1 = cvt4_e4m3(clamp448(v[4] * inv), clamp448(v[5] * inv), clamp448(v[6] * inv), clamp448(v[7] * inv));
     *reinterpret_cast<uint2*>(p.payload + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
+    if (p.deq != nullptr) {  // uniform: the quantized values themselves, as BF16
+      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+      const uint2 lo = fp8x4_scaled_bf16(w0, sc), hi = fp8x4_scaled_bf16(w1, sc);
+      *reinterpret_cast<uint4*>(p.deq + (t * p.num_heads + h) * 128 + sub * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
 
     // gather the 4 block scale bytes of this row into lane 0 of the 16 (all 16 lanes of a row
     // take this branch together: the row decides it)

@@ -143,6 +143,9 @@ int check_attn(const lpfa_attn_args* a) {
   if (!float_finite_positive(a->softmax_scale))
     return fail(LPFA_EINVAL, "softmax_scale must be finite and positive");
   if (float_is_nan(a->fp8_score_guard)) return fail(LPFA_EINVAL, "fp8_score_guard is NaN");
+  if (a->k_deq && (a->q_scale == nullptr || a->k_scale == nullptr || a->pv_mode != LPFA_PV_BF16 || a->qk_bf16))
+    return fail(LPFA_EINVAL, "k_deq needs MX Q and K (q_scale, k_scale) and pv_mode LPFA_PV_BF16");
+  if (a->k_deq && !aligned16(a->k_deq)) return fail(LPFA_EINVAL, "k_deq is not 16-byte aligned");
   if ((a->q_scale == nullptr) != (a->k_scale == nullptr))
     return fail(LPFA_EINVAL, "q_scale and k_scale must both be set (MX mode) or both be NULL (per-tensor mode)");
   if (a->q_scale && (a->cu_scale_q == nullptr || a->cu_scale_k == nullptr))

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.lpfa_abi_version() == 8
+    assert lib.lpfa_abi_version() == 9
 
 
 @pytest.mark.parametrize("cname,pystruct", [("lpfa_attn_args", _lib.AttnArgs), ("lpfa_bwd_args", _lib.BwdArgs)])
@@ -76,13 +76,13 @@ FAKE = 0x10000  # an aligned non-NULL address: validation checks it, nothing der
 def _quant(lib, **kw):
     args = dict(x=FAKE, x_dtype=0, stride_tok=256, stride_head=128, total_tokens=2, num_heads=2, head_dim=128,
                 cu_seqlens=FAKE, cu_scale=FAKE, num_seqs=1, total_scale_rows=128, scaling_mode=0,
-                payload=FAKE, scales=FAKE)
+                payload=FAKE, scales=FAKE, deq=None)
     args.update(kw)
     return lib.mxfp8_quantize_varlen(args["x"], args["x_dtype"], args["stride_tok"], args["stride_head"],
                                      args["total_tokens"], args["num_heads"], args["head_dim"],
                                      args["cu_seqlens"], args["cu_scale"], args["num_seqs"],
                                      args["total_scale_rows"], args["scaling_mode"], args["payload"],
-                                     args["scales"], None, None)
+                                     args["scales"], None, args["deq"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -99,6 +99,7 @@ def _quant(lib, **kw):
     (dict(cu_scale=None), _lib.LPFA_EINVAL),
     (dict(payload=None), _lib.LPFA_EINVAL),
     (dict(scales=FAKE + 1), _lib.LPFA_EINVAL),
+    (dict(deq=FAKE + 8), _lib.LPFA_EINVAL),        # BF16 output not 16-byte aligned
 ])
 def test_quantize_rejects(lib, kw, code):
     assert _quant(lib, **kw) == code
@@ -202,6 +203,9 @@ def _args(**kw):
     (dict(softmax_scale=0.0), _lib.LPFA_EINVAL),
     (dict(softmax_scale=float("nan")), _lib.LPFA_EINVAL),
     (dict(fp8_score_guard=float("nan")), _lib.LPFA_EINVAL),
+    (dict(k_deq=FAKE + 8), _lib.LPFA_EINVAL),       # K's BF16 values not 16-byte aligned
+    (dict(k_deq=FAKE, pv_mode=1), _lib.LPFA_EINVAL),  # only for BF16 V
+    (dict(k_deq=FAKE, q_scale=None, k_scale=None, cu_scale_q=None, cu_scale_k=None), _lib.LPFA_EINVAL),  # MX only
     (dict(softmax_scale=float("inf")), _lib.LPFA_EINVAL),
     (dict(softmax_scale=-0.0), _lib.LPFA_EINVAL),
     (dict(q=None), _lib.LPFA_EINVAL),

@@ -210,6 +210,38 @@ def test_varlen_sampled(tile_order):
     assert_within_bound(out, ref, bound)
 
 
+@pytest.mark.parametrize("case", ["ragged_outliers", "varlen", "ragged_no_outliers"])
+def test_k_deq_same_results(case):
+    """K's BF16 values from the quantizer (`with_deq`) spare the BF16-V kernel's guard-failing tiles
+    their own conversion of K; they hold the same values the tiles would compute (same conversion
+    instruction), so O and LSE are bit-identical with and without them. With them the kernel starts
+    every tile on that path and takes the guard's decision there: the outlier data puts every tile
+    over the guard's bound; without outliers the tiles pass and hand over to the FP8-score path,
+    again with results identical to the run without K's BF16 values."""
+    if case == "varlen":
+        wl = make_workload("varlen", seed=0)
+    elif case == "ragged_outliers":
+        wl = make_custom([300, 1, 130, 64], [129, 257, 5, 400], heads=3, seed=61, outlier_rate=0.01)
+    else:
+        wl = make_custom([300, 1, 130, 64], [129, 257, 5, 400], heads=3, seed=62)
+    dev = torch.device("cuda")
+    mq = lp.VarlenMeta.from_lengths(wl.lengths_q, dev)
+    mk = lp.VarlenMeta.from_lengths(wl.lengths_k, dev)
+    q = lp.quantize_mxfp8_varlen(bf16_to_device(wl.q_bits), mq)
+    k = lp.quantize_mxfp8_varlen(bf16_to_device(wl.k_bits), mk, with_deq=True)
+    v = bf16_to_device(wl.v_bits)
+    out1, lse1 = lp.lp_attn_varlen_fwd(q, k, v, mq, mk, pv_mode="bf16")
+    k_plain = lp.Mxfp8Tensor(k.payload, k.scales, k.meta, k.group_max)
+    out0, lse0 = lp.lp_attn_varlen_fwd(q, k_plain, v, mq, mk, pv_mode="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out0)
+    assert torch.equal(lse1.nan_to_num(), lse0.nan_to_num())
+    if case != "varlen":  # small enough for the oracle everywhere
+        ops = oracle_operands(wl, "bf16")
+        ref = oracle.attention_varlen(ops["qhat"], ops["khat"], ops["vprime"], wl.cu_q, wl.cu_k, pv_mode="bf16")
+        assert_within(compare(out1, lse1, ref), bf16_allowance=True)
+
+
 def test_varlen_fp8_pv_sampled():
     """The outlier varlen workload in the fp8 PV mode (E4M3 V, unscaled E4M3 P). As in the mx
     mode, E4M3 P rounded against the kernel's running maximum and against the oracle's final one

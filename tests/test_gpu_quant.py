@@ -113,6 +113,26 @@ def test_workload_qk(name):
         assert np.array_equal(scales, rs)   # includes the 0x7F pad rows
 
 
+@pytest.mark.parametrize("name", ["tiny", "varlen"])
+def test_deq_output(name):
+    """The quantizer's optional BF16 output (`with_deq`): the quantized values themselves, payload
+    times 2^e, which have at most 4 significant bits and so are exact in BF16 here. Compared bit
+    for bit with the oracle's dequantization of its own quantization; payload and scales are
+    unchanged by the extra output. Pad rows have no tokens and write nothing."""
+    wl = make_workload(name, seed=0)
+    dev = torch.device("cuda")
+    for bits, lengths in ((wl.q_bits, wl.lengths_q), (wl.k_bits, wl.lengths_k)):
+        meta = lp.VarlenMeta.from_lengths(lengths, dev)
+        mx = lp.quantize_mxfp8_varlen(bf16_to_device(bits), meta, with_deq=True)
+        torch.cuda.synchronize()
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        rp, rs, _ = oracle.mx_quantize_varlen(f64(bits), cu, "rceil")
+        assert np.array_equal(mx.payload.cpu().numpy(), rp) and np.array_equal(mx.scales.cpu().numpy(), rs)
+        want = oracle.bf16_round(oracle.mx_dequantize_varlen(rp, rs, cu))
+        got = mx.deq.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, want)
+
+
 def test_cross_keys_full_size():
     """The cross-attention workload's 32768-token key tensor, every byte."""
     wl = make_workload("cross", seed=0)
