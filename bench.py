@@ -48,6 +48,9 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (AMD spec, no spars
 BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBPS = 8000.0
 
+# The PV mode each workload is specified with (the dense shape is run in both; fp8 is its headline)
+DEFAULT_PV_MODE = {"tiny": "bf16", "dense": "fp8", "varlen": "bf16", "pertensor": "fp8", "cross": "fp8", "batch8": "fp8"}
+
 WORKLOAD_TEXT = {
     "tiny": "tiny: 1 sequence x 256 tokens, 2 heads, head_dim 128, noncausal MHA",
     "dense": "dense: 1 sequence x 2048 tokens, 16 heads, head_dim 128, noncausal MHA",
@@ -68,7 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--pv-mode", default="fp8", choices=["bf16", "fp8"])
+    ap.add_argument("--pv-mode", default=None, choices=["bf16", "fp8"],
+                    help="P V mode (default: the workload's own: bf16 for tiny and varlen, fp8 otherwise)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -114,7 +118,7 @@ def main():
     lib = lp.load_library()   # fails loudly if the HIP library is missing
 
     wl = make_workload(args.workload, seed=args.seed)
-    pv_mode = args.pv_mode
+    pv_mode = args.pv_mode or DEFAULT_PV_MODE[args.workload]
     mq = lp.VarlenMeta.from_lengths(wl.lengths_q, dev)
     mk = lp.VarlenMeta.from_lengths(wl.lengths_k, dev)
     up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -249,6 +253,19 @@ def main():
     n_b2b = args.b2b_iters or max(10, min(2000, int(0.5 / max(b2b_ms * 1e-3, 1e-6))))
     if not per_tensor and pv_mode == "fp8" and not args.no_extras:
         extra.update(other_modes(torch, lp, wl, q, k, v, qx, kx, mq, mk, order, out, lse, n_b2b, b2b_ms, flops, up))
+    elif not per_tensor and not args.no_extras:
+        # bf16 PV: the BF16 FlashAttention forward on the same data, back to back (its ceiling)
+        plan_b = lp.AttnPlan(mq, mk, h, pv_mode="bf16", mx=False, qk_bf16=True, tile_order=order)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        plan_b(q, k, v)
+        a_ev.record()
+        for _ in range(n_b2b):
+            plan_b(q, k, v)
+        b_ev.record()
+        torch.cuda.synchronize()
+        bfa_ms = a_ev.elapsed_time(b_ev) / n_b2b
+        extra["attention_bf16_fa_tflops"] = round(flops / (bfa_ms * 1e-3) / 1e12, 2)
+        extra["mxfp8_speedup_vs_bf16_fa"] = round(bfa_ms / b2b_ms, 3)
 
     peaks = None if args.no_extras else measured_peaks(torch, dev)
 
