@@ -877,9 +877,13 @@ struct Attn {
     LDS uint8_t* v_lane = v_lane_addr<1 - PAR>(0);   // V of the previous block
     const int jj = FP8V ? (n16 >> 1) : (n16 >> 2);
     v8i qf[2];
+    v8i kn;   // FP8 scores: the next key tile's fragment and scale, read one slot ahead (their
+    int ksn;  // latency passes under a slot's vector work)
     if (DO_QK && !KB16) {
       qf[0] = q_frag(0);
       qf[1] = q_frag(1);
+      kn = make_v8i(k_a[0], k_b[0]);
+      ksn = MX ? (int)ksc[0] : 127;
     }
     LDS const v8bf* kq[4];  // QB, DQ: this lane's slice-u chunk of key row n16 (row 16t + n16: + t * 4096 bytes)
     if constexpr (KB16) {
@@ -892,6 +896,18 @@ struct Attn {
     float rs[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      // FP8 scores: this slot's key tile fragment was read one slot ahead; key tile k+1's reads go
+      // out now, ahead of this slot's vector work
+      v8i kf;
+      int ks = 127;
+      if (DO_QK && !KB16) {
+        kf = kn;
+        ks = ksn;
+        if (k < 7) {
+          kn = make_v8i(k_a[(k + 1) * 128], k_b[(k + 1) * 128]);  // + 2048 bytes per tile
+          ksn = MX ? (int)ksc[64 * (k + 1)] : 127;
+        }
+      }
       // probabilities of score tile k of block j
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -923,8 +939,6 @@ struct Attn {
         s[k][0] = acc[0];
         s[k][1] = acc[1];
       } else if (DO_QK) {  // scores of block j+1, key tile k (overwrites the consumed tile)
-        const v8i kf = make_v8i(k_a[k * 128], k_b[k * 128]);            // + k * 2048 bytes
-        const int ks = MX ? (int)ksc[64 * k] : 127;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           s[k][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[nt], v4f{0.0f, 0.0f, 0.0f, 0.0f},
