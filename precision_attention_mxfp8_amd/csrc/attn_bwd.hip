@@ -14,11 +14,11 @@
 //  * bwd_dequant_kernel: Qd, Qt, Kd, Vd and Kt dequantized once into BF16 copies in the caller's
 //    workspace (the main kernels re-read every tile once per 64-row block of the other side).
 //    The same launch computes D for every (head, query) into the workspace (16 lanes per row).
-//  * bwd_dkdv_kernel: one workgroup = (128 keys of one sequence, head), 4 waves x 32 keys. The
+//  * bwd_dkdv_kernel: one workgroup = (128 keys of one sequence, head), 8 waves x 16 keys. The
 //    keys' K and V fragments and the dK, dV accumulators stay in registers while the workgroup
 //    walks the sequence's queries 64 at a time. The epilogue writes BF16, or quantizes each
 //    32-element block to MXFP8 with the quantizer's exponent rule (and writes pad scale rows).
-//  * bwd_dq_kernel: one workgroup = (128 queries, head), 4 waves x 32 queries, walking the keys.
+//  * bwd_dq_kernel: one workgroup = (128 queries, head), 8 waves x 16 queries, walking the keys.
 //    dQ has its own pass instead of atomics from the dK/dV pass, so every result is independent
 //    of scheduling; the price is recomputing S and dP.
 //
@@ -39,8 +39,10 @@
 // rows) both spread over the banks. Tiles arrive by 16-byte direct-to-LDS loads from the BF16
 // copies (double-buffered: the next step's tiles load while the current step computes), and
 // fragment reads are issued in groups ahead of the matrix instructions that use them. Each wave
-// owns two 16-row tiles of its own side, so every fragment it reads from LDS feeds two matrix
-// instructions (LDS bandwidth, not the matrix core, bounds a one-tile-per-wave loop).
+// owns NT 16-row tiles of its own side, and each SIMD runs two waves, so that one wave's softmax
+// and LDS waits meet the other's matrix instructions. (Every fragment read from LDS feeds NT
+// matrix instructions: at NT = 1 the loop moves twice the LDS bytes per row that NT = 2 does,
+// which one wave per SIMD needs, and still runs faster.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,8 +63,11 @@ typedef unsigned v4u_t __attribute__((ext_vector_type(4)));  // LDS accesses use
                                                              // uint4 does not bind to LDS references
 
 constexpr int BR = 64;                     // rows of the other side per step (staged tiles)
-constexpr int WR = 32;                     // rows of the workgroup's own side per wave: two 16-row tiles
-constexpr int BO = 4 * WR;                 // own-side rows per workgroup
+constexpr int NW = 8;                      // waves per workgroup: two per SIMD
+constexpr int WR = 16;                     // rows of the workgroup's own side per wave
+constexpr int NT = WR / 16;                // 16-row tiles per wave
+constexpr int BO = NW * WR;                // own-side rows per workgroup
+constexpr int NTHR = 64 * NW;
 constexpr int TILE = BR * 256;             // one staged BF16 tile
 constexpr int STAGE = 3 * TILE;            // the three tiles of one step (double-buffered)
 constexpr int OFF_VEC = 2 * STAGE;         // dK/dV pass: LSE (log2 units) and D of a step's queries, per buffer
@@ -128,12 +133,13 @@ __device__ __forceinline__ void stage_tile(LDS uint8_t* tile, const uint16_t* sr
   const int64_t left = reinterpret_cast<const uint8_t*>(end) - b;
   const int n = left <= 0 ? 0 : (left >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(b), (short)0, n, 0x00020000);
+  constexpr int RW = BR / NW;  // rows per wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < RW / 4; ++i) {
+    const int r = RW * wave + 4 * i + (lane >> 4);
     const int rc = min(r, nrows - 1);
     const uint32_t off = (uint32_t)(rc * H * 256) + 16u * (uint32_t)((lane & 15) ^ (r & 15));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(tile + (16 * wave + 4 * i) * 256), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void*)(tile + (RW * wave + 4 * i) * 256), 16, off, 0, 0, 0);
   }
 }
 
@@ -287,11 +293,11 @@ __device__ __forceinline__ void emit_rows(LDS float* ep, uint8_t* dst, uint8_t* 
   dst_scale[((srow0 + r) * H + head) * 4 + c4] = sbyte;
 }
 
-// accumulators of the wave's two 16-row tiles (result layout: lane (g, c) holds rows 16t + 4g + i
-// of wave w's 32, column 16dt + c) -> FP32 tile of BO rows in LDS, times `mul`
-__device__ __forceinline__ void acc_to_lds(LDS float* ep, const v4f acc[2][8], float mul, int wave, int g, int n16) {
+// accumulators of the wave's 16-row tiles (result layout: lane (g, c) holds rows 16t + 4g + i of
+// wave w's WR, column 16dt + c) -> FP32 tile of BO rows in LDS, times `mul`
+__device__ __forceinline__ void acc_to_lds(LDS float* ep, const v4f acc[NT][8], float mul, int wave, int g, int n16) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -299,12 +305,12 @@ __device__ __forceinline__ void acc_to_lds(LDS float* ep, const v4f acc[2][8], f
 }
 
 // ---- dK, dV
-// One workgroup = BO keys of one (sequence, head); wave w owns keys 32w + 16t + n (t = 0, 1): their
+// One workgroup = BO keys of one (sequence, head); wave w owns keys WR w + 16t + n (t < NT): their
 // K and V fragments and dK, dV accumulators stay in registers while the workgroup walks the
-// sequence's queries 64 at a time. Every fragment read from LDS feeds both key tiles. The next
-// step's Q, dO and Qt tiles load (into the other buffer) while the current step computes.
+// sequence's queries 64 at a time. Every fragment read from LDS feeds the wave's NT key tiles. The
+// next step's Q, dO and Qt tiles load (into the other buffer) while the current step computes.
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTHR) void bwd_dkdv_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_dyn[];
   LDS uint8_t* lds = (LDS uint8_t*)smem_dyn;
 
@@ -321,17 +327,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  v4f dv[2][8], dk[2][8];
+  v4f dv[NT][8], dk[NT][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) dv[t][dt] = dk[t][dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (k_loc < Lk && Lq > 0) {
     // this lane's keys (B operand column n16 of tile t): K and V fragments, k = d
-    v8bf kf[2][4], vf[2][4];
+    v8bf kf[NT][4], vf[NT][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int kr = min(k_loc + WR * wave + 16 * t + n16, Lk - 1);
       const int64_t tk = kbase + kr;
       const uint8_t* kp = p.k + (tk * H + head) * 128 + 8 * g;
@@ -383,9 +389,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
       // S and dP: lane (g, n16) holds key 16t + n16 of the wave, queries 16qt + 4g + i. The
       // fragments of query tile qt+1 are read while the matrix instructions of tile qt run; the
-      // four accumulation chains (S and dP of both key tiles) interleave.
+      // accumulation chains (S and dP of each key tile) interleave.
       // dP starts from -D of its row, so that it ends as dP - D (the workspace holds -D)
-      v4f s[2][4], dp[2][4], nd[4];
+      v4f s[NT][4], dp[NT][4], nd[4];
       v8bf aq[2][4], ao[2][4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) nd[qt] = *reinterpret_cast<LDS v4f*>(vec + BR + 16 * qt + 4 * g);
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NT; ++t) {
             s[t][qt] = mfma(aq[cur][u], kf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][qt]);
             dp[t][qt] = mfma(ao[cur][u], vf[t][u], u == 0 ? nd[qt] : dp[t][qt]);
           }
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         bo[0][i] = col_frag(tdo, 0, i, g, n16);
         bq[0][i] = col_frag(tqt, 0, i, g, n16);
       }
-      uint32_t pw[2][2][4], dw[2][2][4];
+      uint32_t pw[NT][2][4], dw[NT][2][4];
       // LSE in log2 units; on the sequence's last step, +inf past its end (P = 0 there)
       auto probs = [&](auto tail) {
 #pragma unroll
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
             if constexpr (decltype(tail)::value) lv[i] = j * BR + 16 * qt + 4 * g + i < Lq ? lv[i] : __builtin_inff();
           }
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NT; ++t) {
             float pr[4], ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -464,16 +470,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           }
         }
         group_end();
-        v8bf ap[2], ad[2];
+        v8bf ap[NT], ad[NT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
           ap[t] = __builtin_bit_cast(v8bf, make_uint4(pw[t][st][0], pw[t][st][1], pw[t][st][2], pw[t][st][3]));
           ad[t] = __builtin_bit_cast(v8bf, make_uint4(dw[t][st][0], dw[t][st][1], dw[t][st][2], dw[t][st][3]));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NT; ++t) {
             dv[t][d0 + i] = mfma(ap[t], bo[cur][i], dv[t][d0 + i]);
             dk[t][d0 + i] = mfma(ad[t], bq[cur][i], dk[t][d0 + i]);
           }
@@ -488,22 +494,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const bool mx = p.mx_dkv != 0;
   acc_to_lds(ep, dv, 1.0f, wave, g, n16);
   __syncthreads();
-  emit_rows(ep, p.dv, p.dv_scale, mx, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
-  emit_rows(ep + 64 * 128, p.dv, p.dv_scale, mx, p.scaling_mode, kbase + k_loc + 64, srow_k + k_loc + 64, k_loc + 64, Lk,
-            H, head);
+  for (int r0 = 0; r0 < BO; r0 += NTHR / 4)
+    emit_rows(ep + r0 * 128, p.dv, p.dv_scale, mx, p.scaling_mode, kbase + k_loc + r0, srow_k + k_loc + r0, k_loc + r0, Lk,
+              H, head);
   __syncthreads();
   acc_to_lds(ep, dk, p.softmax_scale, wave, g, n16);
   __syncthreads();
-  emit_rows(ep, p.dk, p.dk_scale, mx, p.scaling_mode, kbase + k_loc, srow_k + k_loc, k_loc, Lk, H, head);
-  emit_rows(ep + 64 * 128, p.dk, p.dk_scale, mx, p.scaling_mode, kbase + k_loc + 64, srow_k + k_loc + 64, k_loc + 64, Lk,
-            H, head);
+  for (int r0 = 0; r0 < BO; r0 += NTHR / 4)
+    emit_rows(ep + r0 * 128, p.dk, p.dk_scale, mx, p.scaling_mode, kbase + k_loc + r0, srow_k + k_loc + r0, k_loc + r0, Lk,
+              H, head);
 }
 
 // ---- dQ
-// One workgroup = BO queries of one (sequence, head); wave w owns queries 32w + 16t + n (t = 0, 1)
+// One workgroup = BO queries of one (sequence, head); wave w owns queries WR w + 16t + n (t < NT)
 // and walks the keys 64 at a time, double-buffered like the dK/dV pass.
 
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_dyn[];
   LDS uint8_t* lds = (LDS uint8_t*)smem_dyn;
 
@@ -521,18 +527,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
 
-  v4f dq[2][8];
+  v4f dq[NT][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) dq[t][dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (Lk > 0) {
     // this lane's queries (B operand column n16 of tile t): Q and dO fragments, k = d
-    v8bf qf[2][4], of[2][4];
-    float l2[2], dl[2];
+    v8bf qf[NT][4], of[NT][4];
+    float l2[NT], dl[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int qv = q_loc + WR * wave + 16 * t + n16;
       const int qr = min(qv, Lq - 1);
       const int64_t tq_ = qbase + qr;
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 
       // S^T and dP^T: lane (g, n16) holds query 16t + n16 of the wave, keys 16kt + 4g + i
       // (pipelined like the dK/dV pass)
-      v4f s[2][4], dp[2][4];
+      v4f s[NT][4], dp[NT][4];
       v8bf ak[2][4], av[2][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NT; ++t) {
             s[t][kt] = mfma(ak[cur][u], qf[t][u], u == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t][kt]);
             dp[t][kt] = mfma(av[cur][u], of[t][u], u == 0 ? v4f{dl[t], dl[t], dl[t], dl[t]} : dp[t][kt]);
           }
@@ -604,12 +610,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       v8bf bk[2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) bk[0][i] = col_frag(tkt, 0, i, g, n16);
-      uint32_t dw[2][2][4];
+      uint32_t dw[NT][2][4];
       auto scores_to_ds = [&](auto masked) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < NT; ++t) {
             float ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -632,14 +638,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
           for (int i = 0; i < 4; ++i) bk[cur ^ 1][i] = col_frag(tkt, st1, d1 + i, g, n16);
         }
         group_end();
-        v8bf ad[2];
+        v8bf ad[NT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
           ad[t] = __builtin_bit_cast(v8bf, make_uint4(dw[t][st][0], dw[t][st][1], dw[t][st][2], dw[t][st][3]));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) dq[t][d0 + i] = mfma(ad[t], bk[cur][i], dq[t][d0 + i]);
+          for (int t = 0; t < NT; ++t) dq[t][d0 + i] = mfma(ad[t], bk[cur][i], dq[t][d0 + i]);
         group_end();
       }
       wait_vm_all();
@@ -651,8 +657,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   acc_to_lds(ep, dq, p.softmax_scale, wave, g, n16);
   __syncthreads();
   uint8_t* dqb = reinterpret_cast<uint8_t*>(p.dq);
-  emit_rows(ep, dqb, nullptr, false, 0, qbase + q_loc, 0, q_loc, Lq, H, head);
-  emit_rows(ep + 64 * 128, dqb, nullptr, false, 0, qbase + q_loc + 64, 0, q_loc + 64, Lq, H, head);
+  for (int r0 = 0; r0 < BO; r0 += NTHR / 4)
+    emit_rows(ep + r0 * 128, dqb, nullptr, false, 0, qbase + q_loc + r0, 0, q_loc + r0, Lq, H, head);
 }
 
 }  // namespace
@@ -680,9 +686,9 @@ hipError_t launch_attention_bwd(const BwdParams& p, hipStream_t s) {
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
   if (p.rows_k > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.rows_k / BO * p.num_heads)), dim3(256), LDS_BYTES, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.rows_k / BO * p.num_heads)), dim3(NTHR), LDS_BYTES, s, p);
   if (p.rows_q > 0)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.rows_q / BO * p.num_heads)), dim3(256), LDS_BYTES, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.rows_q / BO * p.num_heads)), dim3(NTHR), LDS_BYTES, s, p);
   return hipGetLastError();
 }
 
