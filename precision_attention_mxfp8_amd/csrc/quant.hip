@@ -6,16 +6,19 @@
 // FastVideo fp8-PV PR (unscaled e4m3 cast of V).
 //
 // Work mapping (HBM-bound, one pass over the input):
-//   A workgroup owns 16 consecutive rows of the scale storage for one head; 16 lanes own one
-//   (scale row, head) pair = 128 elements; each lane loads 8
-//   consecutive elements with one 16-byte load (two for FP32). The 4 lanes of a 32-element
-//   block reduce their maximum with two cross-lane xor steps inside a quad (DPP), derive the
-//   exponent from the maximum's bits, scale by an exact power of two and convert with the
-//   hardware E4M3 conversion (round to nearest even). Lane 0 of the 16 gathers the four scale
-//   bytes and writes them as one word. Pad rows of the scale storage get 0x7F and no payload.
-//   Optionally the workgroup also writes the largest scale byte of its 16 rows' real rows (one
-//   byte per 16-row group and head, 0 for a group of pad rows only): the attention kernel's
-//   precision guard bounds |k| with it.
+//   A workgroup is one wave and owns 16 consecutive rows of the scale storage for one head: a
+//   16-lane row of the wave holds one (scale row, head) pair = 128 elements, 8 consecutive
+//   elements per lane (one 16-byte load, two for FP32), and each lane takes four such rows, so
+//   four loads per lane are in flight before any arithmetic. The 4 lanes of a 32-element block
+//   reduce their maximum with two quad permutations (DPP), derive the exponent from the
+//   maximum's bits, scale by an exact power of two and convert with the hardware E4M3
+//   conversion (round to nearest even). Lane 0 of the 16 gathers the four scale bytes with row
+//   shifts (DPP) and writes them as one word. Pad rows of the scale storage get 0x7F and no
+//   payload. Optionally the wave also writes the largest scale byte of its 16 rows' real rows
+//   (one byte per 16-row group and head, 0 for a group of pad rows only): the attention
+//   kernel's precision guard bounds |k| with it. Every cross-lane step stays inside a 16-lane
+//   row, whose lanes are all real or all pad, except the four reads of the group maximum; no
+//   step goes through LDS and no workgroup waits at a barrier.
 // The token-orientation quantizer (V for the P V product) takes blocks of 32 consecutive
 // tokens of a sequence per (head, column); its mapping is described at the kernel.
 #include <hip/hip_runtime.h>
@@ -56,75 +59,146 @@ struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
   }
 };
 
-// One workgroup's share of the quantizer: 16 rows of the scale storage for one head (`bid`
-// enumerates (16-row group, head) pairs, heads fastest).
+// Cross-lane reads that stay inside 16-lane rows (DPP: no LDS round trip). dpp<CTRL>(x) returns
+// the value x of the lane CTRL names, 0 where that lane lies outside the row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __uint_as_float(dpp<CTRL>(__float_as_uint(x)));
+}
+constexpr int QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]: lane i reads lane i ^ 1
+constexpr int QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]: lane i reads lane i ^ 2
+constexpr int ROW_SHL4 = 0x104;   // row_shl:n: lane i reads lane i + n of its row
+constexpr int ROW_SHL8 = 0x108;
+constexpr int ROW_SHL12 = 0x10C;
+constexpr int ROW_ROR1 = 0x121;   // row_ror:n: lane i reads lane (i - n) mod 16 of its row
+constexpr int ROW_ROR2 = 0x122;
+constexpr int ROW_ROR4 = 0x124;
+constexpr int ROW_ROR8 = 0x128;
+
+constexpr int PREP_THREADS = 64;  // one wave per (16-row group, head)
+
+// A read of the sequence offsets through the constant address space: they do not change while a
+// kernel runs, and with a wave-uniform index this is a scalar load.
+__device__ __forceinline__ int64_t ld_offset(const int32_t* p, int i) {
+  return (int64_t)((const __attribute__((address_space(4))) int32_t*)(uintptr_t)p)[i];
+}
+
+// The largest of four lanes' values: lanes 0, 16, 32 and 48 (one per 16-lane row).
+__device__ __forceinline__ uint32_t max_of_rows(uint32_t x) {
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// One wave's share of the quantizer: the 16 rows of the scale storage of one (16-row group,
+// head). Lane l holds chunk l % 16 of the group's rows l / 16 + 4 i, i = 0..3. `real_rows` of the
+// 16 rows are real (the rest are padding of the sequence's scale storage); FULL: all 16 are, so
+// no per-row test is made. RCEIL: the exponent makes every |x| * 2^-e at most 448, so no clamp.
+// Per-wave bases are scalar and each lane's offsets are formed once, so a row costs one add.
+template <typename T, bool RCEIL, bool FULL>
+__device__ __forceinline__ void quantize_rows(const QuantParams& p, int h, int64_t grp16, int64_t first, int64_t local0,
+                                              int real_rows) {
+  const int64_t H = p.num_heads;
+  const int lane = threadIdx.x, sub = lane & 15, q = lane >> 4;
+  const int64_t row0 = grp16 * 16, tok0 = first + local0;  // tok0: the token of row0 (when it is real)
+
+  // All four loads first. A pad row reads a real row of its sequence instead (the sequence has
+  // at least one token, as it owns scale rows); a pad row's values reach no output, since every
+  // cross-lane step of a row stays inside the row.
+  float v[4][8];
+  if constexpr (FULL) {
+    const T* x0 = static_cast<const T*>(p.x) + tok0 * p.stride_tok + h * p.stride_head;
+    const int64_t off = q * p.stride_tok + sub * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0 + 4 * i * p.stride_tok, off, v[i]);
+  } else {
+    const T* x0 = static_cast<const T*>(p.x) + (real_rows > 0 ? tok0 : first) * p.stride_tok + h * p.stride_head;
+    const int last = real_rows > 0 ? real_rows - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0, (int64_t)min(q + 4 * i, last) * p.stride_tok + sub * 8, v[i]);
+  }
+
+  uint8_t* pay = p.payload + (tok0 * H + h) * 128 + (q * H * 128 + sub * 8);
+  uint8_t* scw = p.scales + (row0 * H + h) * 4 + q * H * 4;
+  uint32_t smax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    // the maximum over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the row)
+    amax = fmaxf(amax, dppf<QUAD_XOR1>(amax));
+    amax = fmaxf(amax, dppf<QUAD_XOR2>(amax));
+    const int e = block_exponent(amax, RCEIL ? LPFA_SCALING_RCEIL : LPFA_SCALING_FLOOR);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 120]: normal
+    const uint32_t sbyte = (uint32_t)(e + 127);
+    // the row's four block scales (lanes 0, 4, 8, 12), gathered into lane 0 of the row
+    const uint32_t word = sbyte | (dpp<ROW_SHL4>(sbyte) << 8) | (dpp<ROW_SHL8>(sbyte) << 16) | (dpp<ROW_SHL12>(sbyte) << 24);
+    uint32_t* scale_word = reinterpret_cast<uint32_t*>(scw + 4 * i * H * 4);
+    if (FULL || q + 4 * i < real_rows) {
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = RCEIL ? v[i][j] * inv : clamp448(v[i][j] * inv);
+      const uint32_t w0 = cvt4_e4m3(y[0], y[1], y[2], y[3]), w1 = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<uint2*>(pay + 4 * i * H * 128) = make_uint2(w0, w1);
+      if (p.deq != nullptr) {  // uniform: the quantized values themselves, as BF16
+        const float sc = __uint_as_float(sbyte << 23);
+        const uint2 a = fp8x4_scaled_bf16(w0, sc), b = fp8x4_scaled_bf16(w1, sc);
+        *reinterpret_cast<uint4*>(p.deq + (tok0 * H + h) * 128 + (q * H * 128 + sub * 8) + 4 * i * H * 128) =
+            make_uint4(a.x, a.y, b.x, b.y);
+      }
+      if (sub == 0) *scale_word = word;
+      smax = max(smax, sbyte);
+    } else if (sub == 0) {
+      *scale_word = 0x7F7F7F7Fu;  // pad row of the 128-row-padded scale storage
+    }
+  }
+
+  if (p.group_max != nullptr) {  // uniform over the wave
+    // each row's largest (over its lanes 0, 4, 8, 12 and, per lane, over its four rows), then the wave's
+    smax = max(smax, dpp<ROW_ROR4>(smax));
+    smax = max(smax, dpp<ROW_ROR8>(smax));
+    const uint32_t g = max_of_rows(smax);
+    if (lane == 0) p.group_max[grp16 * H + h] = (uint8_t)g;
+  }
+}
+
+// One wave's share of the quantizer: the 16 rows of the scale storage of one (16-row group,
+// head) (`bid` enumerates those pairs, heads fastest).
 template <typename T>
-__device__ __forceinline__ void quantize_group(const QuantParams& p, unsigned bid, uint32_t* red) {
+__device__ __forceinline__ void quantize_group(const QuantParams& p, unsigned bid) {
   const int h = (int)(bid % (unsigned)p.num_heads);  // neighbouring workgroups: same rows
   const int64_t grp16 = bid / (unsigned)p.num_heads;  // 16-row group of the scale storage
-  const int sub = threadIdx.x & 15;                           // 8-element chunk of the 128-element row
-  const int64_t srow = grp16 * 16 + (threadIdx.x >> 4);
-
-  // sequence owning this group (groups never straddle sequences: each sequence's scale rows are
-  // padded to a multiple of 128): the largest i with cu_scale[i] <= srow
+  const int64_t row0 = grp16 * 16;
+  // The sequence owning the group, the same for all its rows (every sequence's scale rows are
+  // padded to a multiple of 128, so no group straddles two): the largest i with cu_scale[i] <=
+  // row0. Uniform over the wave, so these reads are scalar loads.
   int lo = 0, hi = p.num_seqs;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if ((int64_t)p.cu_scale[mid] <= srow) lo = mid; else hi = mid;
+    if (ld_offset(p.cu_scale, mid) <= row0) lo = mid; else hi = mid;
   }
-  const int64_t local = srow - p.cu_scale[lo];
-  const int64_t seq_len = (int64_t)p.cu_seqlens[lo + 1] - p.cu_seqlens[lo];
-  uint32_t* scale_word = reinterpret_cast<uint32_t*>(p.scales + (srow * p.num_heads + h) * 4);
-  uint32_t smax = 0;
-  if (local >= seq_len) {  // pad row of the 128-token-padded scale storage
-    if (sub == 0) *scale_word = 0x7F7F7F7Fu;
+  const int64_t local0 = row0 - ld_offset(p.cu_scale, lo);  // the group's first row within its sequence
+  const int64_t first = ld_offset(p.cu_seqlens, lo);
+  const int64_t left = ld_offset(p.cu_seqlens, lo + 1) - first - local0;  // real rows from row0 on
+  const int real_rows = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+  const bool rceil = p.scaling_mode == LPFA_SCALING_RCEIL;
+  if (real_rows == 16) {
+    if (rceil) quantize_rows<T, true, true>(p, h, grp16, first, local0, 16);
+    else quantize_rows<T, false, true>(p, h, grp16, first, local0, 16);
   } else {
-    const int64_t t = p.cu_seqlens[lo] + local;
-    float v[8];
-    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    // reduce over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the 16)
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int e = block_exponent(amax, p.scaling_mode);
-    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 120]: normal
-
-    uint32_t w0 = cvt4_e4m3(clamp448(v[0] * inv), clamp448(v[1] * inv), clamp448(v[2] * inv), clamp448(v[3] * inv));
-    uint32_t w1 = cvt4_e4m3(clamp448(v[4] * inv), clamp448(v[5] * inv), clamp448(v[6] * inv), clamp448(v[7] * inv));
-    *reinterpret_cast<uint2*>(p.payload + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
-    if (p.deq != nullptr) {  // uniform: the quantized values themselves, as BF16
-      const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
-      const uint2 lo = fp8x4_scaled_bf16(w0, sc), hi = fp8x4_scaled_bf16(w1, sc);
-      *reinterpret_cast<uint4*>(p.deq + (t * p.num_heads + h) * 128 + sub * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
-
-    // gather the 4 block scale bytes of this row into lane 0 of the 16 (all 16 lanes of a row
-    // take this branch together: the row decides it)
-    const uint32_t sbyte = (uint32_t)(e + 127);
-    smax = sbyte;
-    const int base = (threadIdx.x & 63) & ~15;
-    uint32_t b1 = __shfl(sbyte, base + 4);
-    uint32_t b2 = __shfl(sbyte, base + 8);
-    uint32_t b3 = __shfl(sbyte, base + 12);
-    if (sub == 0) *scale_word = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-  }
-
-  if (p.group_max != nullptr) {  // uniform over the workgroup
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) smax = max(smax, (uint32_t)__shfl_xor((int)smax, s));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = smax;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      p.group_max[grp16 * p.num_heads + h] = (uint8_t)max(max(red[0], red[1]), max(red[2], red[3]));
+    if (rceil) quantize_rows<T, true, false>(p, h, grp16, first, local0, real_rows);
+    else quantize_rows<T, false, false>(p, h, grp16, first, local0, real_rows);
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(QuantParams p) {
-  __shared__ uint32_t red[4];
-  quantize_group<T>(p, blockIdx.x, red);
+__global__ __launch_bounds__(PREP_THREADS) void mxfp8_quantize_kernel(QuantParams p) {
+  quantize_group<T>(p, blockIdx.x);
 }
 
 // Loads 4 consecutive elements (8 bytes BF16, 16 bytes FP32) as floats.
@@ -226,38 +300,61 @@ __device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
   *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
 }
 
-// The cast by (16-token group, head): a workgroup owns 16 consecutive tokens of one head (bid
-// enumerates (16-token group, head), heads fastest, as the quantizer's groups do), 16 lanes per
-// token as in cast_block. With group maxima (per-tensor K for the attention's precision guard) it
-// also writes the largest code magnitude of its 2048 codes (codes order like magnitudes, and the
-// RNE conversion is monotonic, so that is the code of the largest clamped magnitude). Tokens
-// past the end are not read and count as zero.
-template <typename T>
-__device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid, float* red) {
-  const int h = (int)(bid % (unsigned)p.num_heads);
-  const int64_t t = (int64_t)(bid / (unsigned)p.num_heads) * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+// The cast by (16-token group, head): a workgroup is one wave and owns 16 consecutive tokens of
+// one head (bid enumerates (16-token group, head), heads fastest, as the quantizer's groups do),
+// laid out like the quantizer's rows: lane l holds chunk l % 16 of tokens l / 16 + 4 i. With group
+// maxima (per-tensor K for the attention's precision guard) it also writes the largest code
+// magnitude of its 2048 codes (codes order like magnitudes, and the RNE conversion is monotonic,
+// so that is the code of the largest clamped magnitude). A token past the end reads the group's
+// last real token instead and reaches no output. FULL: all 16 tokens are real.
+template <typename T, bool FULL>
+__device__ __forceinline__ void cast_rows(const CastParams& p, int h, int64_t g16) {
+  const int64_t H = p.num_heads, t0 = g16 * 16;
+  const int lane = threadIdx.x, sub = lane & 15, q = lane >> 4;
+  // all four loads first; a token past the end reads the group's last real token instead
+  const int n = FULL ? 16 : (int)(p.total_tokens - t0);  // real tokens in the group (>= 1)
+  const T* x0 = static_cast<const T*>(p.x) + t0 * p.stride_tok + h * p.stride_head;
+  float v[4][8];
+  if constexpr (FULL) {
+    const int64_t off = q * p.stride_tok + sub * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0 + 4 * i * p.stride_tok, off, v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0, (int64_t)min(q + 4 * i, n - 1) * p.stride_tok + sub * 8, v[i]);
+  }
+  uint8_t* y = p.y + (t0 * H + h) * 128 + (q * H * 128 + sub * 8);
   float m = 0.0f;
-  if (t < p.total_tokens) {
-    float v[8];
-    Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = clamp448(v[i]);
-      m = fmaxf(m, fabsf(v[i]));
+  for (int i = 0; i < 4; ++i) {
+    float mi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[i][j] = clamp448(v[i][j]);
+      mi = fmaxf(mi, fabsf(v[i][j]));
     }
-    const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
-    *reinterpret_cast<uint2*>(p.y + (t * p.num_heads + h) * 128 + sub * 8) = make_uint2(w0, w1);
+    if (FULL || q + 4 * i < n) {
+      m = fmaxf(m, mi);
+      const uint32_t w0 = cvt4_e4m3(v[i][0], v[i][1], v[i][2], v[i][3]), w1 = cvt4_e4m3(v[i][4], v[i][5], v[i][6], v[i][7]);
+      *reinterpret_cast<uint2*>(y + 4 * i * H * 128) = make_uint2(w0, w1);
+    }
   }
-  if (p.group_max == nullptr) return;  // uniform over the workgroup
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float g = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    p.group_max[(int64_t)(bid / (unsigned)p.num_heads) * p.num_heads + h] = (uint8_t)(cvt_pk_e4m3(g, 0.0f) & 0x7Fu);
-  }
+  if (p.group_max == nullptr) return;  // uniform over the wave
+  // the row's largest (rotations by 1, 2, 4 and 8 reach all 16 lanes), then the wave's
+  m = fmaxf(m, dppf<ROW_ROR1>(m));
+  m = fmaxf(m, dppf<ROW_ROR2>(m));
+  m = fmaxf(m, dppf<ROW_ROR4>(m));
+  m = fmaxf(m, dppf<ROW_ROR8>(m));
+  const float g = __uint_as_float(max_of_rows(__float_as_uint(m)));  // non-negative: ordered like its bits
+  if (lane == 0) p.group_max[g16 * H + h] = (uint8_t)(cvt_pk_e4m3(g, 0.0f) & 0x7Fu);
+}
+
+template <typename T>
+__device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid) {
+  const int h = (int)(bid % (unsigned)p.num_heads);
+  const int64_t g16 = bid / (unsigned)p.num_heads;
+  if (g16 * 16 + 16 <= p.total_tokens) cast_rows<T, true>(p, h, g16);
+  else cast_rows<T, false>(p, h, g16);
 }
 
 template <typename T>
@@ -266,9 +363,8 @@ __global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void e4m3_cast_gmax_kernel(CastParams p) {
-  __shared__ float red[4];
-  cast_group<T>(p, blockIdx.x, red);
+__global__ __launch_bounds__(PREP_THREADS) void e4m3_cast_gmax_kernel(CastParams p) {
+  cast_group<T>(p, blockIdx.x);
 }
 
 // The three preparation passes of a forward in one launch: Q's and K's MXFP8 quantization and
@@ -279,14 +375,12 @@ __global__ __launch_bounds__(256) void e4m3_cast_gmax_kernel(CastParams p) {
 // is a multiple of 8 every head's Q, K and V codes are written by workgroups of one XCD (ids are
 // dealt round-robin over the 8 XCDs), the XCD whose L2 the attention kernel reads that head from.
 template <typename T>
-__global__ __launch_bounds__(256) void prepare_qkv_kernel(QuantParams pq, QuantParams pk, CastParams pv, unsigned nq,
-                                                          unsigned nk) {
-  __shared__ uint32_t red[4];
-  __shared__ float fred[4];
+__global__ __launch_bounds__(PREP_THREADS) void prepare_qkv_kernel(QuantParams pq, QuantParams pk, CastParams pv,
+                                                                   unsigned nq, unsigned nk) {
   const unsigned b = blockIdx.x;
-  if (b < nq) quantize_group<T>(pq, b, red);
-  else if (b < nq + nk) quantize_group<T>(pk, b - nq, red);
-  else cast_group<T>(pv, b - nq - nk, fred);
+  if (b < nq) quantize_group<T>(pq, b);
+  else if (b < nq + nk) quantize_group<T>(pk, b - nq);
+  else cast_group<T>(pv, b - nq - nk);
 }
 
 // ---- per-tensor current scaling (TensorRT-LLM TE-backend PR: Q/K/V and O scales written from
@@ -413,9 +507,9 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
   if (groups == 0) return hipSuccess;
   const dim3 grid((unsigned)groups);
   if (p.x_dtype == LPFA_DTYPE_BF16)
-    hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, dim3(PREP_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -436,9 +530,9 @@ hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, cons
   if (nq + nk + nv == 0) return hipSuccess;
   const dim3 grid((unsigned)(nq + nk + nv));
   if (pq.x_dtype == LPFA_DTYPE_BF16)
-    hipLaunchKernelGGL(prepare_qkv_kernel<uint16_t>, grid, dim3(256), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
+    hipLaunchKernelGGL(prepare_qkv_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
   else
-    hipLaunchKernelGGL(prepare_qkv_kernel<float>, grid, dim3(256), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
+    hipLaunchKernelGGL(prepare_qkv_kernel<float>, grid, dim3(PREP_THREADS), 0, s, pq, pk, pv, (unsigned)nq, (unsigned)nk);
   return hipGetLastError();
 }
 
@@ -448,9 +542,9 @@ hipError_t launch_cast(const CastParams& p, hipStream_t s) {
   if (p.group_max != nullptr) {
     const dim3 grid((unsigned)((p.total_tokens + 15) / 16 * p.num_heads));
     if (p.x_dtype == LPFA_DTYPE_BF16)
-      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, p);
     else
-      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<float>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<float>, grid, dim3(PREP_THREADS), 0, s, p);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((threads + 255) / 256));
