@@ -59,11 +59,35 @@ struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
   }
 };
 
+// An 8-element chunk as loaded (one 16-byte word for BF16, two for FP32), and its values.
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* p, uint4 w[sizeof(T) / 2]) {
+#pragma unroll
+  for (int k = 0; k < (int)sizeof(T) / 2; ++k) w[k] = reinterpret_cast<const uint4*>(p)[k];
+}
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(const uint4 w[sizeof(T) / 2], float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(u[i]);
+      v[2 * i + 1] = bf16_hi(u[i]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      v[4 * k] = __uint_as_float(w[k].x); v[4 * k + 1] = __uint_as_float(w[k].y);
+      v[4 * k + 2] = __uint_as_float(w[k].z); v[4 * k + 3] = __uint_as_float(w[k].w);
+    }
+  }
+}
+
 // Cross-lane reads that stay inside 16-lane rows (DPP: no LDS round trip). dpp<CTRL>(x) returns
 // the value x of the lane CTRL names, 0 where that lane lies outside the row.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
@@ -94,11 +118,36 @@ __device__ __forceinline__ uint32_t max_of_rows(uint32_t x) {
   return max(max(a, b), max(c, d));
 }
 
+// Four BF16 (two words) -> four E4M3 codes of x / 2^e in one word, first element in the low byte,
+// with the hardware's scaled conversion; `scale` is 2^e built from the E8M0 byte (byte << 23, the
+// zero pattern for e = -127). Checked on the GPU against the RNE conversion of x * 2^-e for every
+// finite BF16 x and every e in [-127, 120] with |x| / 2^e <= 448: identical. Above 448 it gives NaN
+// where the clamped path saturates, so only the RCEIL exponent (quotients <= 448) uses it.
+__device__ __forceinline__ uint32_t cvt4_bf16_scaled(uint32_t w0, uint32_t w1, float scale) {
+  typedef short v2s_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  v2s_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s_t{0, 0}, __builtin_bit_cast(v2bf_t, w0), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf_t, w1), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// The largest magnitude of eight BF16 (four words), as the float it stands for: magnitudes of
+// finite BF16 order like their 15-bit patterns, so a packed 16-bit integer maximum finds it.
+__device__ __forceinline__ float bf16x8_amax(uint4 w) {
+  typedef unsigned short v2u16_t __attribute__((ext_vector_type(2)));
+  const uint32_t M = 0x7FFF7FFFu;
+  const v2u16_t a = __builtin_bit_cast(v2u16_t, w.x & M), b = __builtin_bit_cast(v2u16_t, w.y & M);
+  const v2u16_t c = __builtin_bit_cast(v2u16_t, w.z & M), d = __builtin_bit_cast(v2u16_t, w.w & M);
+  const v2u16_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return __uint_as_float(max((uint32_t)m[0], (uint32_t)m[1]) << 16);
+}
+
 // One wave's share of the quantizer: the 16 rows of the scale storage of one (16-row group,
 // head). Lane l holds chunk l % 16 of the group's rows l / 16 + 4 i, i = 0..3. `real_rows` of the
 // 16 rows are real (the rest are padding of the sequence's scale storage); FULL: all 16 are, so
-// no per-row test is made. RCEIL: the exponent makes every |x| * 2^-e at most 448, so no clamp.
-// Per-wave bases are scalar and each lane's offsets are formed once, so a row costs one add.
+// no per-row test is made. RCEIL: the exponent makes every |x| * 2^-e at most 448, so no clamp,
+// and BF16 input converts with the scaled conversion straight from its bits (no unpacking and no
+// multiplies). Per-wave bases are scalar and each lane's offsets are formed once.
 template <typename T, bool RCEIL, bool FULL>
 __device__ __forceinline__ void quantize_rows(const QuantParams& p, int h, int64_t grp16, int64_t first, int64_t local0,
                                               int real_rows) {
@@ -109,27 +158,35 @@ __device__ __forceinline__ void quantize_rows(const QuantParams& p, int h, int64
   // All four loads first. A pad row reads a real row of its sequence instead (the sequence has
   // at least one token, as it owns scale rows); a pad row's values reach no output, since every
   // cross-lane step of a row stays inside the row.
-  float v[4][8];
+  constexpr int NW = sizeof(T) / 2;  // 16-byte words per 8-element chunk
+  uint4 raw[4][NW];
   if constexpr (FULL) {
     const T* x0 = static_cast<const T*>(p.x) + tok0 * p.stride_tok + h * p.stride_head;
     const int64_t off = q * p.stride_tok + sub * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0 + 4 * i * p.stride_tok, off, v[i]);
+    for (int i = 0; i < 4; ++i) load_chunk<T>(x0 + 4 * i * p.stride_tok + off, raw[i]);
   } else {
     const T* x0 = static_cast<const T*>(p.x) + (real_rows > 0 ? tok0 : first) * p.stride_tok + h * p.stride_head;
     const int last = real_rows > 0 ? real_rows - 1 : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0, (int64_t)min(q + 4 * i, last) * p.stride_tok + sub * 8, v[i]);
+    for (int i = 0; i < 4; ++i) load_chunk<T>(x0 + (int64_t)min(q + 4 * i, last) * p.stride_tok + sub * 8, raw[i]);
   }
+  constexpr bool SCALED_CVT = RCEIL && sizeof(T) == 2;
 
   uint8_t* pay = p.payload + (tok0 * H + h) * 128 + (q * H * 128 + sub * 8);
   uint8_t* scw = p.scales + (row0 * H + h) * 4 + q * H * 4;
   uint32_t smax = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float v[8];
     float amax = 0.0f;
+    if constexpr (SCALED_CVT) {
+      amax = bf16x8_amax(raw[i][0]);
+    } else {
+      unpack_chunk<T>(raw[i], v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    }
     // the maximum over the 4 lanes of the 32-element block (lanes 4b..4b+3 of the row)
     amax = fmaxf(amax, dppf<QUAD_XOR1>(amax));
     amax = fmaxf(amax, dppf<QUAD_XOR2>(amax));
@@ -140,10 +197,18 @@ __device__ __forceinline__ void quantize_rows(const QuantParams& p, int h, int64
     const uint32_t word = sbyte | (dpp<ROW_SHL4>(sbyte) << 8) | (dpp<ROW_SHL8>(sbyte) << 16) | (dpp<ROW_SHL12>(sbyte) << 24);
     uint32_t* scale_word = reinterpret_cast<uint32_t*>(scw + 4 * i * H * 4);
     if (FULL || q + 4 * i < real_rows) {
-      float y[8];
+      uint32_t w0, w1;
+      if constexpr (SCALED_CVT) {
+        const float sc = __uint_as_float(sbyte << 23);  // 2^e
+        w0 = cvt4_bf16_scaled(raw[i][0].x, raw[i][0].y, sc);
+        w1 = cvt4_bf16_scaled(raw[i][0].z, raw[i][0].w, sc);
+      } else {
+        float y[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = RCEIL ? v[i][j] * inv : clamp448(v[i][j] * inv);
-      const uint32_t w0 = cvt4_e4m3(y[0], y[1], y[2], y[3]), w1 = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+        for (int j = 0; j < 8; ++j) y[j] = RCEIL ? v[j] * inv : clamp448(v[j] * inv);
+        w0 = cvt4_e4m3(y[0], y[1], y[2], y[3]);
+        w1 = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+      }
       *reinterpret_cast<uint2*>(pay + 4 * i * H * 128) = make_uint2(w0, w1);
       if (p.deq != nullptr) {  // uniform: the quantized values themselves, as BF16
         const float sc = __uint_as_float(sbyte << 23);
@@ -306,8 +371,9 @@ __device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
 // maxima (per-tensor K for the attention's precision guard) it also writes the largest code
 // magnitude of its 2048 codes (codes order like magnitudes, and the RNE conversion is monotonic,
 // so that is the code of the largest clamped magnitude). A token past the end reads the group's
-// last real token instead and reaches no output. FULL: all 16 tokens are real.
-template <typename T, bool FULL>
+// last real token instead and reaches no output. FULL: all 16 tokens are real; GMAX: the group
+// maxima are written (p.group_max is set).
+template <typename T, bool FULL, bool GMAX>
 __device__ __forceinline__ void cast_rows(const CastParams& p, int h, int64_t g16) {
   const int64_t H = p.num_heads, t0 = g16 * 16;
   const int lane = threadIdx.x, sub = lane & 15, q = lane >> 4;
@@ -331,15 +397,15 @@ __device__ __forceinline__ void cast_rows(const CastParams& p, int h, int64_t g1
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       v[i][j] = clamp448(v[i][j]);
-      mi = fmaxf(mi, fabsf(v[i][j]));
+      if (GMAX) mi = fmaxf(mi, fabsf(v[i][j]));
     }
     if (FULL || q + 4 * i < n) {
-      m = fmaxf(m, mi);
+      if (GMAX) m = fmaxf(m, mi);
       const uint32_t w0 = cvt4_e4m3(v[i][0], v[i][1], v[i][2], v[i][3]), w1 = cvt4_e4m3(v[i][4], v[i][5], v[i][6], v[i][7]);
       *reinterpret_cast<uint2*>(y + 4 * i * H * 128) = make_uint2(w0, w1);
     }
   }
-  if (p.group_max == nullptr) return;  // uniform over the wave
+  if (!GMAX) return;
   // the row's largest (rotations by 1, 2, 4 and 8 reach all 16 lanes), then the wave's
   m = fmaxf(m, dppf<ROW_ROR1>(m));
   m = fmaxf(m, dppf<ROW_ROR2>(m));
@@ -353,8 +419,14 @@ template <typename T>
 __device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid) {
   const int h = (int)(bid % (unsigned)p.num_heads);
   const int64_t g16 = bid / (unsigned)p.num_heads;
-  if (g16 * 16 + 16 <= p.total_tokens) cast_rows<T, true>(p, h, g16);
-  else cast_rows<T, false>(p, h, g16);
+  const bool full = g16 * 16 + 16 <= p.total_tokens;
+  if (p.group_max != nullptr) {
+    if (full) cast_rows<T, true, true>(p, h, g16);
+    else cast_rows<T, false, true>(p, h, g16);
+  } else {
+    if (full) cast_rows<T, true, false>(p, h, g16);
+    else cast_rows<T, false, false>(p, h, g16);
+  }
 }
 
 template <typename T>
