@@ -8,8 +8,10 @@
 //     instruction of the attention's FP8 score and P V products, on register operands.
 //   peak_mfma_bf16(waves_per_simd, iters, out, stream): the same with v_mfma_f32_16x16x32_bf16
 //     (16384 FLOP each), the instruction of the BF16 paths.
-//   peak_copy(src, dst, bytes, stream): dst = src with 16-byte nontemporal loads and stores, 8 in
-//     flight per thread, grid-stride; moves 2 * bytes through HBM.
+//   peak_copy(src, dst, bytes, stream): dst = src (bytes a multiple of 16), one 16-byte
+//     nontemporal load and store per thread, one workgroup per 4 KiB; moves 2 * bytes through HBM.
+//     Measured on 1 GiB: 6.6 TB/s, against 4.7-4.8 TB/s for a grid-stride loop of 4096 workgroups
+//     with 8 chunks in flight per thread, and 5.1-5.7 TB/s for 2 or 4 chunks per thread.
 // The matrix kernels launch 256 CUs x 4 SIMDs x waves_per_simd waves; `out` (one float per wave,
 // device memory) receives a sum of the accumulators so the work cannot be dropped.
 #include <hip/hip_runtime.h>
@@ -59,23 +61,13 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* out) {
   if (lane == 0) out[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s;
 }
 
-// Each thread moves 8 independent 16-byte chunks per round (8 loads in flight, then 8 stores);
-// whole rounds need no bounds checks, the tail is handled chunk by chunk.
+// One 16-byte chunk per thread: a grid of bytes / 4096 workgroups keeps every CU's queue of
+// workgroups full until the end.
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rounds = n / (8 * stride);
-  for (int64_t r = 0; r < rounds; ++r) {
-    const int64_t base = r * 8 * stride + tid;
-    v4u v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + base + u * stride);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(v[u], dst + base + u * stride);
-  }
-  for (int64_t i = rounds * 8 * stride + tid; i < n; i += stride) dst[i] = src[i];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
@@ -97,8 +89,10 @@ int peak_mfma_bf16(int waves_per_simd, int iters, float* out, void* stream) {
 
 // bytes must be a multiple of 16; src and dst 16-byte aligned.
 int peak_copy(const void* src, void* dst, int64_t bytes, void* stream) {
-  const int64_t n = bytes / 16;
-  hipLaunchKernelGGL(copy_kernel, dim3(NUM_CU * 16), dim3(256), 0, static_cast<hipStream_t>(stream),
+  const int64_t n = bytes / 16, blocks = (n + 255) / 256;
+  if (bytes % 16 != 0 || blocks > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+  if (blocks == 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const v4u*>(src), static_cast<v4u*>(dst), n);
   return (int)hipGetLastError();
 }
