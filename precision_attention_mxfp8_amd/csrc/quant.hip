@@ -11,10 +11,11 @@
 //   elements per lane (one 16-byte load, two for FP32), and each lane takes four such rows, so
 //   four loads per lane are in flight before any arithmetic. The 4 lanes of a 32-element block
 //   reduce their maximum with two quad permutations (DPP), derive the exponent from the
-//   maximum's bits, scale by an exact power of two and convert with the hardware E4M3
-//   conversion (round to nearest even). Lane 0 of the 16 gathers the four scale bytes with row
-//   shifts (DPP) and writes them as one word. Pad rows of the scale storage get 0x7F and no
-//   payload. Optionally the wave also writes the largest scale byte of its 16 rows' real rows
+//   maximum's bits and convert x * 2^-e to E4M3 with round to nearest even: BF16 input under
+//   RCEIL with the scaled BF16 conversion straight from its bits, otherwise by multiplying with
+//   an exact power of two and converting the product. Lane 0 of the 16 gathers the four scale
+//   bytes with row shifts (DPP) and writes them as one word. Pad rows of the scale storage get
+//   0x7F and no payload. Optionally the wave also writes the largest scale byte of its 16 rows' real rows
 //   (one byte per 16-row group and head, 0 for a group of pad rows only): the attention
 //   kernel's precision guard bounds |k| with it. Every cross-lane step stays inside a 16-lane
 //   row, whose lanes are all real or all pad, except the four reads of the group maximum; no
