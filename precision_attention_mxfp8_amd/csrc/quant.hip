@@ -60,11 +60,19 @@ struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
   }
 };
 
-// An 8-element chunk as loaded (one 16-byte word for BF16, two for FP32), and its values.
+// An 8-element chunk as loaded (one 16-byte word for BF16, two for FP32), and its values. The
+// quantizer and the cast by groups read their input once, with nontemporal loads: the input then
+// does not displace from the L2 caches the codes these kernels write, which the attention reads
+// next (one-launch preparation + attention at the dense shape: 35.56 -> 34.94 us per step; the
+// preparation alone, replayed back to back, then reads its input from HBM: 5.8 -> 4.7 TB/s).
 template <typename T>
 __device__ __forceinline__ void load_chunk(const T* p, uint4 w[sizeof(T) / 2]) {
+  typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int k = 0; k < (int)sizeof(T) / 2; ++k) w[k] = reinterpret_cast<const uint4*>(p)[k];
+  for (int k = 0; k < (int)sizeof(T) / 2; ++k) {
+    const v4u_t x = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p) + k);
+    w[k] = make_uint4(x.x, x.y, x.z, x.w);
+  }
 }
 template <typename T>
 __device__ __forceinline__ void unpack_chunk(const uint4 w[sizeof(T) / 2], float v[8]) {
@@ -381,15 +389,18 @@ __device__ __forceinline__ void cast_rows(const CastParams& p, int h, int64_t g1
   // all four loads first; a token past the end reads the group's last real token instead
   const int n = FULL ? 16 : (int)(p.total_tokens - t0);  // real tokens in the group (>= 1)
   const T* x0 = static_cast<const T*>(p.x) + t0 * p.stride_tok + h * p.stride_head;
-  float v[4][8];
+  uint4 raw[4][sizeof(T) / 2];
   if constexpr (FULL) {
     const int64_t off = q * p.stride_tok + sub * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0 + 4 * i * p.stride_tok, off, v[i]);
+    for (int i = 0; i < 4; ++i) load_chunk<T>(x0 + 4 * i * p.stride_tok + off, raw[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Loader<T>::load8(x0, (int64_t)min(q + 4 * i, n - 1) * p.stride_tok + sub * 8, v[i]);
+    for (int i = 0; i < 4; ++i) load_chunk<T>(x0 + (int64_t)min(q + 4 * i, n - 1) * p.stride_tok + sub * 8, raw[i]);
   }
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) unpack_chunk<T>(raw[i], v[i]);
   uint8_t* y = p.y + (t0 * H + h) * 128 + (q * H * 128 + sub * 8);
   float m = 0.0f;
 #pragma unroll
