@@ -474,7 +474,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prepare_qkv_kernel(QuantParams p
 // workgroup of the cast reduces those partial maxima before casting (work[0] receives amax).
 constexpr int AMAX_BLOCKS = 256;
 
-__device__ __forceinline__ int amax_blocks(int64_t chunks) {
+__host__ __device__ __forceinline__ int amax_blocks(int64_t chunks) {
   const int64_t b = (chunks + 255) / 256;
   return (int)(b < AMAX_BLOCKS ? b : AMAX_BLOCKS);
 }
@@ -484,59 +484,114 @@ __global__ __launch_bounds__(256) void amax_kernel(CastParams p) {
   __shared__ float red[4];
   const int64_t chunks = p.total_tokens * p.num_heads * 16;  // 8-element chunks
   const int64_t stride = (int64_t)gridDim.x * 256;
+  constexpr int U = 8;  // independent 16-byte loads in flight per thread (FP32: 16)
+  // a packed tensor (heads and tokens back to back) is one run of chunks: no index arithmetic
+  const bool packed = p.stride_head == 128 && p.stride_tok == (int64_t)p.num_heads * 128;
   float m = 0.0f;
-  // a stride loop with 4 independent 16-byte loads in flight per thread
-  for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < chunks; c0 += 4 * stride) {
-    float v[4][8];
+  for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < chunks; c0 += U * stride) {
+    uint4 raw[U][sizeof(T) / 2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       int64_t c = c0 + u * stride;
       c = c < chunks ? c : c0;  // a chunk past the end rereads this thread's first one (no effect on the max)
-      const int64_t head_row = c >> 4;
-      const int64_t t = head_row / p.num_heads;
-      const int h = (int)(head_row - t * p.num_heads);
-      Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + (c & 15) * 8, v[u]);
+      int64_t off = c * 8;
+      if (!packed) {
+        const int64_t head_row = c >> 4;
+        const int64_t t = head_row / p.num_heads;
+        const int h = (int)(head_row - t * p.num_heads);
+        off = t * p.stride_tok + h * p.stride_head + (c & 15) * 8;
+      }
+#pragma unroll
+      for (int k = 0; k < (int)sizeof(T) / 2; ++k) raw[u][k] = reinterpret_cast<const uint4*>(static_cast<const T*>(p.x) + off)[k];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u) {
+      float v[8];
+      unpack_chunk<T>(raw[u], v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  m = fmaxf(m, dppf<ROW_ROR1>(m));
+  m = fmaxf(m, dppf<ROW_ROR2>(m));
+  m = fmaxf(m, dppf<ROW_ROR4>(m));
+  m = fmaxf(m, dppf<ROW_ROR8>(m));
+  m = __uint_as_float(max_of_rows(__float_as_uint(m)));  // non-negative: ordered like its bits
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) p.amax[1 + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void cast_current_kernel(CastParams p) {
-  __shared__ float red[4];
-  const int64_t chunks = p.total_tokens * p.num_heads * 16;
-  const int nb = chunks > 0 ? amax_blocks(chunks) : 0;
-  float m = (int)threadIdx.x < nb ? p.amax[1 + threadIdx.x] : 0.0f;
+// The scaled cast by (16-token group, head), one wave each, laid out like the cast by groups: lane
+// l holds chunk l % 16 of tokens l / 16 + 4 i. The wave's loads go out first; it then reduces the
+// partial maxima itself (four per lane, DPP within rows, one read per row), so no workgroup waits
+// at a barrier before its loads.
+template <typename T, bool FULL>
+__device__ __forceinline__ void cast_current_rows(const CastParams& p, int h, int64_t g16, int nb) {
+  const int64_t H = p.num_heads, t0 = g16 * 16;
+  const int lane = threadIdx.x, sub = lane & 15, q = lane >> 4;
+  const int n = FULL ? 16 : (int)(p.total_tokens - t0);  // real tokens in the group (>= 1)
+  const T* x0 = static_cast<const T*>(p.x) + t0 * p.stride_tok + h * p.stride_head;
+  uint4 raw[4][sizeof(T) / 2];
+  if constexpr (FULL) {
+    const int64_t off = q * p.stride_tok + sub * 8;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < (int)sizeof(T) / 2; ++k)
+        raw[i][k] = reinterpret_cast<const uint4*>(x0 + 4 * i * p.stride_tok + off)[k];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < (int)sizeof(T) / 2; ++k)
+        raw[i][k] = reinterpret_cast<const uint4*>(x0 + (int64_t)min(q + 4 * i, n - 1) * p.stride_tok + sub * 8)[k];
+  }
+  // amax over the partial maxima (at most 256: four per lane)
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * lane + j;
+    if (b < nb) m = fmaxf(m, p.amax[1 + b]);
+  }
+  m = fmaxf(m, dppf<ROW_ROR1>(m));
+  m = fmaxf(m, dppf<ROW_ROR2>(m));
+  m = fmaxf(m, dppf<ROW_ROR4>(m));
+  m = fmaxf(m, dppf<ROW_ROR8>(m));
+  const float amax = __uint_as_float(max_of_rows(__float_as_uint(m)));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE division (round to nearest)
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid == 0) {
+  if (g16 == 0 && h == 0 && lane == 0) {
     p.amax[0] = amax;
     *p.descale = s;
   }
-  const int64_t head_row = gid >> 4;
-  if (head_row >= p.total_tokens * p.num_heads) return;
-  const int64_t t = head_row / p.num_heads;
-  const int h = (int)(head_row - t * p.num_heads);
-  const int sub = threadIdx.x & 15;
-  float v[8];
-  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
+  uint8_t* y = p.y + (t0 * H + h) * 128 + (q * H * 128 + sub * 8);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = clamp448(v[i] / s);  // the quotient rounded to float32 first
-  const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
-  *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
+  for (int i = 0; i < 4; ++i) {
+    if (!FULL && q + 4 * i >= n) continue;
+    float v[8];
+    unpack_chunk<T>(raw[i], v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = clamp448(v[j] / s);  // the quotient rounded to float32 first
+    const uint32_t w0 = cvt4_e4m3(v[0], v[1], v[2], v[3]), w1 = cvt4_e4m3(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<uint2*>(y + 4 * i * H * 128) = make_uint2(w0, w1);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(PREP_THREADS) void cast_current_kernel(CastParams p) {
+  const int64_t chunks = p.total_tokens * p.num_heads * 16;
+  const int nb = chunks > 0 ? amax_blocks(chunks) : 0;
+  if (chunks == 0) {  // an empty tensor: amax 0, descale 1
+    if (threadIdx.x == 0) {
+      p.amax[0] = 0.0f;
+      *p.descale = 1.0f;
+    }
+    return;
+  }
+  const int h = (int)(blockIdx.x % (unsigned)p.num_heads);
+  const int64_t g16 = blockIdx.x / (unsigned)p.num_heads;
+  if (g16 * 16 + 16 <= p.total_tokens) cast_current_rows<T, true>(p, h, g16, nb);
+  else cast_current_rows<T, false>(p, h, g16, nb);
 }
 
 // Scratch of the allocation-free current-scaling entry point: the partial maxima that
@@ -574,14 +629,16 @@ hipError_t current_scratch(float** out, int* capacity) {
 
 hipError_t launch_cast_current(const CastParams& p, hipStream_t s) {
   const int64_t chunks = p.total_tokens * p.num_heads * 16;
-  const dim3 grid((unsigned)(chunks > 0 ? (chunks + 255) / 256 : 1));  // one block writes descale
-  const dim3 agrid((unsigned)(grid.x < (unsigned)AMAX_BLOCKS ? grid.x : (unsigned)AMAX_BLOCKS));
+  // the cast: one wave per (16-token group, head); an empty tensor still gets one (it writes the
+  // descale)
+  const dim3 grid((unsigned)(chunks > 0 ? (p.total_tokens + 15) / 16 * p.num_heads : 1));
+  const dim3 agrid((unsigned)(chunks > 0 ? amax_blocks(chunks) : 0));
   if (p.x_dtype == LPFA_DTYPE_BF16) {
     if (chunks > 0) hipLaunchKernelGGL(amax_kernel<uint16_t>, agrid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(cast_current_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(cast_current_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, p);
   } else {
     if (chunks > 0) hipLaunchKernelGGL(amax_kernel<float>, agrid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(cast_current_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(cast_current_kernel<float>, grid, dim3(PREP_THREADS), 0, s, p);
   }
   return hipGetLastError();
 }
