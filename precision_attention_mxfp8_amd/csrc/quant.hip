@@ -34,32 +34,6 @@ namespace lpfa {
 
 namespace {
 
-template <typename T>
-struct Loader;
-
-template <>
-struct Loader<uint16_t> {  // BF16 bit patterns: 8 elements = one 16-byte load
-  __device__ static void load8(const void* base, int64_t off, float v[8]) {
-    uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
-    uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(u[i]);
-      v[2 * i + 1] = bf16_hi(u[i]);
-    }
-  }
-};
-
-template <>
-struct Loader<float> {  // FP32: 8 elements = two 16-byte loads
-  __device__ static void load8(const void* base, int64_t off, float v[8]) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
 // An 8-element chunk as loaded (one 16-byte word for BF16, two for FP32), and its values. The
 // quantizer and the cast by groups read their input once, with nontemporal loads: the input then
 // does not displace from the L2 caches the codes these kernels write, which the attention reads
@@ -359,21 +333,6 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_tokens_kernel(QuantParams 
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void cast_block(const CastParams& p, unsigned bid) {
-  const int64_t gid = (int64_t)bid * 256 + threadIdx.x;
-  const int64_t head_row = gid >> 4;
-  const int sub = threadIdx.x & 15;
-  if (head_row >= p.total_tokens * p.num_heads) return;
-  const int64_t t = head_row / p.num_heads;
-  const int h = (int)(head_row - t * p.num_heads);
-  float v[8];
-  Loader<T>::load8(p.x, t * p.stride_tok + h * p.stride_head + sub * 8, v);
-  uint32_t w0 = cvt4_e4m3(clamp448(v[0]), clamp448(v[1]), clamp448(v[2]), clamp448(v[3]));
-  uint32_t w1 = cvt4_e4m3(clamp448(v[4]), clamp448(v[5]), clamp448(v[6]), clamp448(v[7]));
-  *reinterpret_cast<uint2*>(p.y + head_row * 128 + sub * 8) = make_uint2(w0, w1);
-}
-
 // The cast by (16-token group, head): a workgroup is one wave and owns 16 consecutive tokens of
 // one head (bid enumerates (16-token group, head), heads fastest, as the quantizer's groups do),
 // laid out like the quantizer's rows: lane l holds chunk l % 16 of tokens l / 16 + 4 i. With group
@@ -442,12 +401,7 @@ __device__ __forceinline__ void cast_group(const CastParams& p, unsigned bid) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void e4m3_cast_kernel(CastParams p) {
-  cast_block<T>(p, blockIdx.x);
-}
-
-template <typename T>
-__global__ __launch_bounds__(PREP_THREADS) void e4m3_cast_gmax_kernel(CastParams p) {
+__global__ __launch_bounds__(PREP_THREADS) void e4m3_cast_kernel(CastParams p) {
   cast_group<T>(p, blockIdx.x);
 }
 
@@ -678,21 +632,13 @@ hipError_t launch_prepare_qkv(const QuantParams& pq, const QuantParams& pk, cons
 }
 
 hipError_t launch_cast(const CastParams& p, hipStream_t s) {
-  const int64_t threads = p.total_tokens * p.num_heads * 16;
-  if (threads == 0) return hipSuccess;
-  if (p.group_max != nullptr) {
-    const dim3 grid((unsigned)((p.total_tokens + 15) / 16 * p.num_heads));
-    if (p.x_dtype == LPFA_DTYPE_BF16)
-      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, p);
-    else
-      hipLaunchKernelGGL(e4m3_cast_gmax_kernel<float>, grid, dim3(PREP_THREADS), 0, s, p);
-    return hipGetLastError();
-  }
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.total_tokens * p.num_heads == 0) return hipSuccess;
+  // one wave per (16-token group, head), with or without group maxima
+  const dim3 grid((unsigned)((p.total_tokens + 15) / 16 * p.num_heads));
   if (p.x_dtype == LPFA_DTYPE_BF16)
-    hipLaunchKernelGGL(e4m3_cast_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(e4m3_cast_kernel<uint16_t>, grid, dim3(PREP_THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(e4m3_cast_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(e4m3_cast_kernel<float>, grid, dim3(PREP_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
