@@ -1147,6 +1147,46 @@ struct Attn {
 
   // O d tiles DT0..DT1-1 = O^T / (rounded sum) * vd -> BF16; with LSE, also
   // LSE = ln2 * (m + log2 l).
+  // Two-group kernel: this group's half of O (d tiles DT0..DT0+3 = 64 columns) for the wave's 32
+  // queries, staged through the group's V object (free once the key loop is over: every wave
+  // has passed the merge barrier) so that each store writes 8 whole 128-byte row halves instead
+  // of 16 32-byte pieces. Row r of the stage holds query wave*32 + r; its 16-byte chunk c sits at
+  // chunk c ^ (r & 7).
+  template <int DT0>
+  __device__ __forceinline__ void epilogue_staged(float vd, bool with_lse) {
+    const int q0 = qtile0 * BM;
+    LDS uint8_t* stg = vobj[DT0 == 0 ? 0 : 1] + wave * 4096;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float lt = l_run[nt] + __shfl_xor(l_run[nt], 16);
+      lt += __shfl_xor(lt, 32);
+      const int r = nt * 16 + n16;
+      const int qi = q0 + wave * 32 + r;
+      const float ls = o_sum[nt][0];
+      const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const v4f x = o[DT0 + d][nt];
+        const uint32_t u = (uint32_t)(4 * d + g) ^ (uint32_t)(2 * (r & 7));  // 8-byte unit in the row
+        *reinterpret_cast<LDS v2u_t*>(stg + r * 128 + u * 8) =
+            v2u_t{cvt_pk_bf16((x[0] * inv) * vd, (x[1] * inv) * vd), cvt_pk_bf16((x[2] * inv) * vd, (x[3] * inv) * vd)};
+      }
+      if (with_lse && g == 0 && qi < Lq)
+        p.lse[(int64_t)head * p.total_q + q_start + qi] =
+            lt > 0.0f ? (m_run[nt] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+    }
+    const int c = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + (lane >> 3);
+      const v4u_t w = *reinterpret_cast<LDS const v4u_t*>(stg + r * 128 + ((c ^ (r & 7)) << 4));
+      const int qi = q0 + wave * 32 + r;
+      if (qi < Lq)
+        *reinterpret_cast<uint4*>(p.out + ((int64_t)(q_start + qi) * H + head) * 128 + 16 * DT0 + 8 * c) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+
   template <int DT0, int DT1>
   __device__ __forceinline__ void epilogue(float vd, bool with_lse) {
     const int q0 = qtile0 * BM;
@@ -1408,10 +1448,10 @@ struct Attn {
       __syncthreads();
       if (grp == 0) {
         merge_half<0>(take, xtake[0], xtake[64]);
-        epilogue<0, 4>(vd, true);
+        epilogue_staged<0>(vd, true);
       } else {
         merge_half<1>(take, xtake[0], xtake[64]);
-        epilogue<4, 8>(vd, false);
+        epilogue_staged<4>(vd, false);
       }
       return true;
     }
