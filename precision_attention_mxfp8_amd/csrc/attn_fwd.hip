@@ -1187,6 +1187,43 @@ struct Attn {
     }
   }
 
+  // One-group kernel: the same staging for whole rows. Each wave writes its 32 queries' BF16 rows
+  // (256 bytes) into 8 KB of V object 0 (the caller's barrier has ended every wave's V reads;
+  // 16-byte chunk c of row r at c ^ (r & 15)) and stores them as 4 whole rows per instruction.
+  __device__ __forceinline__ void epilogue_staged_rows(float vd) {
+    const int q0 = qtile0 * BM;
+    LDS uint8_t* stg = vobj[0] + wave * 8192;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float lt = l_run[nt] + __shfl_xor(l_run[nt], 16);
+      lt += __shfl_xor(lt, 32);
+      const int r = nt * 16 + n16;
+      const int qi = q0 + wave * 32 + r;
+      const float ls = o_sum[nt][0];
+      const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4f x = o[dt][nt];
+        const uint32_t u = (uint32_t)(4 * dt + g) ^ (uint32_t)(2 * (r & 15));  // 8-byte unit in the row
+        *reinterpret_cast<LDS v2u_t*>(stg + r * 256 + u * 8) =
+            v2u_t{cvt_pk_bf16((x[0] * inv) * vd, (x[1] * inv) * vd), cvt_pk_bf16((x[2] * inv) * vd, (x[3] * inv) * vd)};
+      }
+      if (g == 0 && qi < Lq)
+        p.lse[(int64_t)head * p.total_q + q_start + qi] =
+            lt > 0.0f ? (m_run[nt] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+    }
+    const int c = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + (lane >> 4);
+      const v4u_t w = *reinterpret_cast<LDS const v4u_t*>(stg + r * 256 + ((c ^ (r & 15)) << 4));
+      const int qi = q0 + wave * 32 + r;
+      if (qi < Lq)
+        *reinterpret_cast<uint4*>(p.out + ((int64_t)(q_start + qi) * H + head) * 128 + 8 * c) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+
   template <int DT0, int DT1>
   __device__ __forceinline__ void epilogue(float vd, bool with_lse) {
     const int q0 = qtile0 * BM;
@@ -1456,7 +1493,13 @@ struct Attn {
       return true;
     }
     if (G == 2 && grp == 1) return true;  // no key block: group 0 writes zeros and -inf
-    epilogue<0, 8>(vd, true);
+    if constexpr (G == 1) {
+      wait_vm_all();
+      __syncthreads();  // every wave's last V reads are done: V object 0 becomes the stage
+      epilogue_staged_rows(vd);
+    } else {
+      epilogue<0, 8>(vd, true);
+    }
     return true;
   }
 };
