@@ -1145,8 +1145,7 @@ struct Attn {
       }
   }
 
-  // O d tiles DT0..DT1-1 = O^T / (rounded sum) * vd -> BF16; with LSE, also
-  // LSE = ln2 * (m + log2 l).
+  // O = O^T / (rounded sum) * vd -> BF16 and LSE = ln2 * (m + log2 l), as in epilogue() below.
   // Two-group kernel: this group's half of O (d tiles DT0..DT0+3 = 64 columns) for the wave's 32
   // queries, staged through the group's V object (free once the key loop is over: every wave
   // has passed the merge barrier) so that each store writes 8 whole 128-byte row halves instead
@@ -1224,6 +1223,8 @@ struct Attn {
     }
   }
 
+  // O d tiles DT0..DT1-1 = O^T / (rounded sum) * vd -> BF16; with LSE, also
+  // LSE = ln2 * (m + log2 l). (The two-group kernel's path for a tile with no key block.)
   template <int DT0, int DT1>
   __device__ __forceinline__ void epilogue(float vd, bool with_lse) {
     const int q0 = qtile0 * BM;
