@@ -12,9 +12,11 @@ metadata is built once, before timing.
 Prints ONE JSON line:
 * value = attention FLOPs (4 * Lq * Lk * H * D summed over sequences) per second of whole step,
   over exactly --steps steps after --warmup untimed ones (nothing is stamped inside them);
-* roofline = the attention kernel's own rate, from a labelled pass after the timed steps in which
-  every attention dispatch stamps a HIP event pair at its start and end (hipExtLaunchKernel),
-  --stamped samples, against the dense FP8 matrix peak (published, and measured: measured_peaks);
+* roofline = the attention kernel's own rate: its FLOPs over its average launch duration, the
+  mean per-launch time of the protocol pass below (HIP events on the launching stream around
+  batches of back-to-back forwards), against the dense FP8 matrix peak (published, and measured:
+  measured_peaks); beside it, a labelled pass after the timed steps in which every attention
+  dispatch stamps a HIP event pair at its start and end (hipExtLaunchKernel, --stamped samples);
 * protocol = the LP-FA4 README's benchmark protocol ("Benchmark reproduction"): operands quantized
   once, the forward alone back to back, 1 s of warmup, then a 5 s window of event-timed batches
   (each >= 1 ms); raw per-launch samples, the padded scale offsets, the workload and the
