@@ -220,7 +220,7 @@ struct Attn {
   using L = Lay<FP8V, KB16>;
   using PF = PFrag<FP8V>;
   static constexpr int G = Groups<FP8V>::G;
-  static constexpr bool QREG = G == 2 && !VMX;  // FP8 Q fragments in registers (q_frags)
+  static constexpr bool QREG = G == 2;  // FP8 Q fragments in registers (q_frags)
 
   // ---- per-workgroup constants ----
   const AttnParams& p;
@@ -245,7 +245,7 @@ struct Attn {
 
   // ---- per-wave state ----
   int qsc[2];
-  v8i qreg[2];  // two-group kernel with unscaled-P V: this wave's FP8 Q fragments, held in registers
+  v8i qreg[2];  // two-group kernel: this wave's FP8 Q fragments, held in registers
   v8bf qb16[2][4];           // QB, DQ: Q fragments, query tile nt, head_dim slice 32u .. 32u + 31
   uint4 kpre[4];             // DQ: this lane's staged K chunks of the next block (FP8), and
   uint32_t kpre_sc[4];       // their rows' scale words
@@ -525,9 +525,9 @@ struct Attn {
   }
 
   // ---------------------------------------------------------------- scores
-  // The score instructions' Q operands: held in registers by the two-group kernel (except with
-  // MX V, whose extra scale registers leave no room; 16 KB less LDS read per key block and wave,
-  // 26.9 -> 26.3 us at the dense 2048 x 16 shape), else read from LDS.
+  // The score instructions' Q operands: held in registers by the two-group kernel (16 KB less
+  // LDS read per key block and wave: 26.9 -> 26.3 us at the dense 2048 x 16 shape, 27.4 -> 26.5 us
+  // with MX V), else read from LDS.
   __device__ __forceinline__ void q_frags(v8i qf[2]) const {
     if constexpr (QREG) {
       qf[0] = qreg[0];
