@@ -571,3 +571,53 @@ def test_fp8_score_guard_threshold_selects_the_path(pv_mode):
     with pytest.raises(ValueError):
         _run_mx(wl, pv_mode, fp8_score_guard=0.0)
 
+
+
+# ---------------------------------------------------------------- a sequence with queries but no keys
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "bf16_fa"])
+def test_sequence_without_keys_through_the_abi(mode):
+    """The C ABI's contract for a sequence with queries but no keys: its O rows are 0 and its LSE is
+    -inf, while the other sequences are unaffected. The Python wrapper rejects such metadata (the
+    pages define no result for it), so the plan is built on metadata with one key there and its
+    struct is then pointed at the real, keyless key offsets: the call itself goes through
+    lp_attn_varlen_fwd as any caller of the library would make it. Covers the one-group kernel
+    (bf16 PV, BF16 FlashAttention forward) and the two-group kernel (fp8 PV)."""
+    from helpers import f64
+    lq, lk, h = [130, 40, 200], [150, 0, 90], 2
+    wl = make_custom(lq, lk, heads=h, seed=77)
+    dev = torch.device("cuda")
+    mq = lp.VarlenMeta.from_lengths(lq, dev)
+    mk = lp.VarlenMeta.from_lengths(lk, dev)
+    mk_one = lp.VarlenMeta.from_lengths([150, 1, 90], dev)
+    qb, kb, vb = bf16_to_device(wl.q_bits), bf16_to_device(wl.k_bits), bf16_to_device(wl.v_bits)
+    if mode == "bf16_fa":
+        plan = lp.AttnPlan(mq, mk_one, h, pv_mode="bf16", mx=False, qk_bf16=True)
+        q, k, v = qb, kb, vb
+    else:
+        plan = lp.AttnPlan(mq, mk_one, h, pv_mode=mode)
+        q, k = lp.quantize_mxfp8_varlen(qb, mq), lp.quantize_mxfp8_varlen(kb, mk)
+        v = lp.cast_e4m3(vb) if mode == "fp8" else vb
+        plan._args.cu_scale_k = mk.cu_scale.data_ptr()
+    a = plan._args
+    a.cu_seqlens_k = mk.cu_seqlens.data_ptr()
+    a.total_k, a.max_seqlen_k = mk.total_tokens, mk.max_seqlen
+    plan.meta_k, plan._kshape = mk, (mk.total_tokens, h, 128)
+    plan._keep = plan._keep + (mk,)
+    plan.out.fill_(1.0)
+    plan.lse.fill_(1.0)
+    out, lse = plan(q, k, v)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.all(o[130:170] == 0.0)
+    assert np.all(np.isneginf(l[:, 130:170]))
+    # the other two sequences against the oracle, computed on them alone
+    pv = "bf16" if mode == "bf16_fa" else mode
+    if mode == "bf16_fa":
+        qhat, khat, vprime = f64(wl.q_bits), f64(wl.k_bits), f64(wl.v_bits)
+    else:
+        ops = oracle_operands(wl, pv)
+        qhat, khat, vprime = ops["qhat"], ops["khat"], ops["vprime"]
+    keep = np.r_[0:130, 170:370]
+    ref = oracle.attention_varlen(qhat[keep], khat, vprime, [0, 130, 330], [0, 150, 240], pv_mode=pv)
+    st = compare(out[torch.as_tensor(keep, device=out.device)], lse[:, torch.as_tensor(keep, device=lse.device)], ref)
+    assert_within(st)
